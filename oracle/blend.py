@@ -93,7 +93,8 @@ def k_deviation(k_new: np.ndarray, k_old: np.ndarray) -> np.ndarray:
 
 def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.ndarray,
                 n_ctx: int, s_in: np.ndarray, x_in: np.ndarray, k_out: int,
-                rowwise: bool = False, store: Optional[str] = None) -> Dict[str, np.ndarray]:
+                rowwise: bool = False, store: Optional[str] = None,
+                keep: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """One layer of selective recompute.
 
     k_cache, v_cache [T][n_kv][hd]: this layer's cache (keys already moved to
@@ -105,7 +106,11 @@ def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.
 
     Returns k_cache, v_cache (new K/V written for every row of s_in), dev
     [m_in] (NaN on query rows), sel (positions into s_in), s_out = s_in[sel]
-    and y [m_out][d], the layer output of the kept rows in s_out order."""
+    and y [m_out][d], the layer output of the kept rows in s_out order.
+
+    keep: optional teacher forcing of step 4 -- ascending positions into s_in
+    of the candidate rows to keep instead of the top-k by deviation (used to
+    compare another implementation on the same selection)."""
     s_in = np.asarray(s_in, dtype=np.int64)
     T = k_cache.shape[0]
     if np.any(np.diff(s_in) <= 0):
@@ -126,7 +131,12 @@ def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.
     kc[s_in] = k
     vc[s_in] = v
     # 4. keep the HKVD rows plus the query rows
-    keep = cand[topk_hkvd(dev[cand], min(k_out, len(cand)))]
+    if keep is None:
+        keep = cand[topk_hkvd(dev[cand], min(k_out, len(cand)))]
+    else:
+        keep = np.asarray(keep, dtype=np.int64)
+        if not np.all(np.isin(keep, cand)) or np.any(np.diff(keep) <= 0):
+            raise ValueError("keep must be ascending candidate positions")
     sel = np.concatenate([keep, np.nonzero(s_in >= n_ctx)[0]])
     s_out = s_in[sel]
     # 5. attention of the kept rows over the blended cache, causal
@@ -169,8 +179,8 @@ def assemble_caches(cfg, chunk_kv: Dict[int, tuple], order: Sequence[int], T: in
     return K, V
 
 
-def shift_caches(cfg, K: Sequence[np.ndarray], offsets) -> List[np.ndarray]:
-    return [rope_shift(k, offsets, cfg.rope_theta) for k in K]
+def shift_caches(cfg, K: Sequence[np.ndarray], offsets, store: Optional[str] = None) -> List[np.ndarray]:
+    return [rope_shift(k, offsets, cfg.rope_theta, store) for k in K]
 
 
 def blend_stack(ws: Sequence[Dict[str, np.ndarray]], cfg, K: Sequence[np.ndarray], V: Sequence[np.ndarray],

@@ -26,18 +26,7 @@ from typing import Dict, Optional
 import numpy as np
 
 from .rope import apply_rope
-
-
-def round_store(x: np.ndarray, store: str) -> np.ndarray:
-    """Round to the storage dtype ('f32', 'f64' = no rounding, 'bf16' = RNE)."""
-    if store in ("f32", "f64", None):
-        return x
-    if store != "bf16":
-        raise ValueError(store)
-    dt = x.dtype
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32).astype(dt)
+from .storage import round_store  # noqa: F401  (re-exported)
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:

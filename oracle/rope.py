@@ -21,6 +21,8 @@ import math
 
 import numpy as np
 
+from .storage import round_store
+
 
 def inv_freq(theta: float, head_dim: int) -> list:
     """theta_i = base^(-2i/hd) in fp64, i = 0 .. hd/2 - 1."""
@@ -74,14 +76,16 @@ def apply_rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
     return rotate(x, cos, sin)
 
 
-def rope_shift(k_cache: np.ndarray, chunk_offsets, theta: float) -> np.ndarray:
+def rope_shift(k_cache: np.ndarray, chunk_offsets, theta: float, store=None) -> np.ndarray:
     """Re-rotate the cached keys of every chunk to its new absolute offset.
 
     k_cache [T][n_kv][hd] holds, for chunk c, keys rotated at local positions
     0 .. L_c-1 (precomputed in isolation).  Chunk c starts at row o_c, so its
     rows are rotated once more by delta = o_c.  Chunk 0 (delta = 0) and rows
-    after the last chunk (the query) are returned unchanged.  Returns a new
-    array; V needs no correction and is not an argument."""
+    after the last chunk (the query) are returned unchanged.  The rotated rows
+    are written back to the cache, so they are rounded to its storage dtype
+    (``store``: None / 'f32' keep fp32, 'bf16' rounds to nearest even).
+    Returns a new array; V needs no correction and is not an argument."""
     out = k_cache.copy()
     offs = [int(o) for o in chunk_offsets]
     for c in range(1, len(offs) - 1):
@@ -90,5 +94,5 @@ def rope_shift(k_cache: np.ndarray, chunk_offsets, theta: float) -> np.ndarray:
             continue
         delta = np.full(hi - lo, lo, dtype=np.int64)
         cos, sin = rope_table(theta, k_cache.shape[-1], delta)
-        out[lo:hi] = rotate(k_cache[lo:hi], cos, sin)
+        out[lo:hi] = round_store(rotate(k_cache[lo:hi], cos, sin), store)
     return out
