@@ -1,0 +1,251 @@
+"""Throughput of the CacheBlend fusor layer on one MI355X.
+
+Workload: the Llama-3-8B-shaped bf16 layer (d_model 4096, 32 query / 8 KV
+heads of 128, FFN 14336, RoPE base 500000) with 6 retrieved chunks of 512
+tokens and a 32-token query (3104 tokens), recompute ratio r = 0.15 (461
+HKVD tokens + 32 query rows).  Weights N(0, 0.02) and chunk / query
+embeddings N(0, 1) are seeded synthetic values; the cached K/V of each chunk
+come from an isolated prefill at position 0 and the hidden states from a full
+prefill of the same layer (set-up, untimed, on the GPU).
+
+One step is one fusor layer: the RoPE re-alignment of that layer's cached
+keys (cb_rope_shift) followed by the selective recompute of the HKVD rows
+(cb_blend_layer: gather + RMSNorm, QKV with RoPE, K deviation and K/V
+scatter, top-k, partial causal GQA attention, O projection, SwiGLU MLP).
+value = context tokens blended per second = T / step time.
+
+Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--extra", action="store_true", help="also time the select call and full prefill")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_flops(p, m_in, m_out, positions):
+    d, q, kv, F = p.d_model, p.q_dim, p.kv_dim, p.ffn_dim
+    g = {"gemm_qkv": 2 * m_in * d * (q + 2 * kv), "gemm_o": 2 * m_out * q * d,
+         "gemm_gateup": 2 * m_out * d * 2 * F, "gemm_down": 2 * m_out * F * d}
+    g["attention"] = int(4 * p.head_dim * p.n_q_heads * np.sum(np.asarray(positions, np.int64) + 1))
+    return g
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    F.lib()   # fails loudly when the library is missing
+    log("library loaded; generating inputs")
+    p = synth.PRESETS["llama8b_layer"]
+    seed = args.seed
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    cfg = F.config_of(p)
+    T, n_ctx, d, kvd = p.T, p.n_ctx, p.d_model, p.kv_dim
+    order = synth.chunk_order(p, seed)
+    offs = synth.chunk_offsets(p, order)
+    L0 = int(offs[1])
+    n_cand = n_ctx - L0
+    k = F.num_selected(p.r_e4, n_ctx, n_cand)
+
+    # ---------------- set-up (untimed) ----------------
+    w = synth.layer_weights(p, seed, 0)
+    layer = F.DeviceLayer(cfg, w, dev)
+    del w
+    rope = F.DeviceRope(cfg, T, dev)
+    ws = F.workspace(cfg, T, T, dev)
+    e_all = torch.from_numpy(synth.context_embeddings(p, seed, order)).to(dev, bf)
+    k_pre = torch.zeros((T, kvd), dtype=bf, device=dev)
+    v_pre = torch.zeros((T, kvd), dtype=bf, device=dev)
+    for c in range(p.n_chunks):
+        lo, hi = int(offs[c]), int(offs[c + 1])
+        L = hi - lo
+        h_iso = torch.empty((L, d), dtype=bf, device=dev)
+        kt = torch.empty((L, kvd), dtype=bf, device=dev)
+        vt = torch.empty((L, kvd), dtype=bf, device=dev)
+        F.full_prefill_layer(cfg, layer, rope, e_all[lo:hi].contiguous(), L, 0, kt, vt, h_iso, ws)
+        h2 = torch.empty_like(h_iso)
+        F.full_prefill_layer(cfg, layer, rope, h_iso, L, 0, k_pre[lo:hi], v_pre[lo:hi], h2, ws)
+    h_full = torch.empty((T, d), dtype=bf, device=dev)
+    kf = torch.empty((T, kvd), dtype=bf, device=dev)
+    vf = torch.empty((T, kvd), dtype=bf, device=dev)
+    F.full_prefill_layer(cfg, layer, rope, e_all, T, 0, kf, vf, h_full, ws)
+    # select call: recompute all candidates once, keep the HKVD set S
+    k_cache = k_pre.clone()
+    v_cache = v_pre.clone()
+    F.rope_shift(cfg, rope, k_cache, T * kvd, 1, T, offs)
+    s_all = torch.arange(L0, T, dtype=torch.int32, device=dev)
+    m_sel = F.expected_m_out(T, n_ctx, T - L0, k)
+    s_sel = torch.empty(m_sel, dtype=torch.int32, device=dev)
+    h_sel = torch.empty((m_sel, d), dtype=bf, device=dev)
+    dv_all = torch.empty(T - L0, dtype=torch.float32, device=dev)
+    F.blend_layer(cfg, layer, rope, k_cache, v_cache, T, n_ctx, L0, s_all, T - L0, h_full, s_all, k, h_sel, dv_all,
+                  s_sel, ws)
+    torch.cuda.synchronize()
+    S = s_sel.clone()
+    m = m_sel
+    hout = torch.empty((m, d), dtype=bf, device=dev)
+    s_out = torch.empty(m, dtype=torch.int32, device=dev)
+    dv = torch.empty(m, dtype=torch.float32, device=dev)
+    # the step works on its own copies of the cache; repeated steps rotate the
+    # same rows again and rewrite the same recomputed rows, at identical cost
+    kb = k_pre.clone()
+    vb = v_cache.clone()
+
+    def step():
+        F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
+        F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, h_full, S, k, hout, dv, s_out, ws)
+
+    log(f"set-up done (k={k}, m={m}); timing {args.steps} steps after {args.warmup} warm-up steps")
+    # ---------------- timed region ----------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations: the same steps again with hipEvents around every launch
+    F.profile_begin()
+    for _ in range(args.steps):
+        step()
+    stats = F.profile_end()
+    torch.cuda.synchronize()
+    positions = s_out.cpu().numpy()
+    flops = layer_flops(p, m, m, positions)
+    kern = {}
+    for name, st in stats.items():
+        avg = st["total_ms"] / st["launches"]
+        e = {"avg_ms": round(avg, 5), "launches_per_step": st["launches"] // args.steps}
+        if name in flops:
+            tf = flops[name] / (avg * 1e-3) / 1e12
+            e.update({"tflops": round(tf, 1), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)})
+        kern[name] = e
+    shift_bytes = 2 * n_cand * kvd * 2
+    if "rope_shift" in kern:
+        gbs = shift_bytes / (kern["rope_shift"]["avg_ms"] * 1e-3) / 1e9
+        kern["rope_shift"].update({"gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    dom = "gemm_gateup"
+    dom_ms = kern[dom]["avg_ms"]
+    dom_tf = flops[dom] / (dom_ms * 1e-3) / 1e12
+    total_flops = sum(flops.values())
+
+    extra = {}
+    if args.extra:
+        # select call (recompute all candidates + top-k) and full prefill of the same layer
+        kk, vv = k_cache.clone(), v_cache.clone()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            F.blend_layer(cfg, layer, rope, kk, vv, T, n_ctx, L0, s_all, T - L0, h_full, s_all, k, h_sel, dv_all,
+                          s_sel, ws)
+        torch.cuda.synchronize()
+        extra["select_call_ms"] = round((time.perf_counter() - t0) * 100, 4)
+        h2 = torch.empty((T, d), dtype=bf, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            F.full_prefill_layer(cfg, layer, rope, h_full, T, 0, kf, vf, h2, ws)
+        torch.cuda.synchronize()
+        extra["full_prefill_ms"] = round((time.perf_counter() - t0) * 100, 4)
+
+    cpu = None
+    log(f"gpu timing done: {ms:.4f} ms/step")
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(p, seed, k, args.cpu_seconds)
+
+    out = {
+        "metric": "blended-context tokens/s at r=0.15 (Llama-8B-shaped layer)",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) embeddings; cached KV from isolated prefill)",
+        "config": {"workload": "llama8b_layer: 6x512-token chunks + 32-token query (T=3104), r=0.15, "
+                               "k=461 HKVD + 32 query rows; d=4096, 32q/8kv heads x128, ffn 14336",
+                   "T": T, "k": k, "m": m, "step": "cb_rope_shift + cb_blend_layer"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops[dom]},
+        "layer_tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
+        "layer_frac_mfma": round(total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels": kern,
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out))
+
+
+def cpu_baseline(p, seed, k, budget_s):
+    """The oracle's blend call (numpy fp32) on the host cores, same shapes."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import blend
+    from rag_kv_cache_layer_amd import synth
+    T, n_ctx = p.T, p.n_ctx
+    L0 = p.chunk_lens[0]
+    w = synth.layer_weights(p, seed, 0)
+    K = synth.random_normal(p, seed, (T, p.n_kv_heads, p.head_dim), tag_layer=11)
+    V = synth.random_normal(p, seed, (T, p.n_kv_heads, p.head_dim), tag_layer=12)
+    x = synth.random_normal(p, seed, (T, p.d_model), tag_layer=13)
+    S = np.concatenate([synth.random_subset(p, seed, L0, n_ctx, k), np.arange(n_ctx, T)]).astype(np.int64)
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 20):
+        t0 = time.perf_counter()
+        blend.blend_layer(w, p, K, V, n_ctx, S, x[S], k, store="bf16")
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(T / t, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} oracle blend calls (numpy fp32, {threads} BLAS threads) of the same layer "
+                      f"and shapes, median {t * 1e3:.0f} ms"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * cacheblend.h -- C ABI of the CacheBlend per-layer KV fusor for MI355X (gfx950).
+ *
+ * The fusor is the GPU part of CacheBlend ("CacheBlend: Fast Large Language
+ * Model Serving for RAG with Cached Knowledge Fusion", arXiv 2405.16444).
+ * Every retrieved chunk has a KV cache computed on its own at positions
+ * 0 .. L_c-1.  At query time the chunks are laid out in context order, the
+ * cached keys are moved to their new absolute positions, and on every layer
+ * a small set of tokens is recomputed (section 4.2, Figure 5b): the layer
+ * input is masked down to the selected tokens, their Q/K/V are computed, the
+ * K/V of the other tokens are reused from the cache, and attention of the
+ * selected tokens over all tokens produces the next layer's input.  The
+ * tokens are the ones with the highest KV deviation (HKVD, section 4.3),
+ * narrowed gradually from layer to layer (section 4.3, Figure 9).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Geometry.  The context is n_chunks chunks in context order followed by
+ *    the query.  Row (token) j of the context has global position j.  Chunk c
+ *    occupies rows [o_c, o_{c+1}) with o_0 = 0 and o_{n_chunks} = n_ctx; the
+ *    query rows are [n_ctx, T).  The first chunk is the prefix: its cached KV
+ *    is exact and it is never re-rotated nor recomputed.  The candidate rows
+ *    for recomputation are [first_chunk_len, n_ctx).
+ *  - Tensors are row-major.  Caches are [T][n_kv_heads][head_dim]; hidden
+ *    states are [rows][d_model]; weights are in nn.Linear layout
+ *    [out_features][in_features]: w_q [n_q*hd][d], w_k/w_v [n_kv*hd][d],
+ *    w_o [d][n_q*hd], w_gate/w_up [ffn][d], w_down [d][ffn].  Element type is
+ *    cb_layer_config.dtype (bf16 or fp32) for weights, caches and hidden
+ *    states; RMSNorm gains and RoPE tables are always fp32.
+ *  - RoPE (section 4.3, footnote 3, and the aifetchly guide, "RoPE Delta
+ *    Positional Realignment"): interleaved pairs (2i, 2i+1) of every head are
+ *    rotated by angle p*theta_i, theta_i = rope_theta^(-2i/hd).  Kernels read
+ *    cos/sin from a device table cb_rope_dev built by cb_rope_table on the
+ *    host (fp64 angle, C library cos/sin, rounded once to fp32).
+ *  - Pointers marked "device" are HIP device pointers; "host" pointers are
+ *    read before the call returns.  The library allocates no memory: every
+ *    buffer, including the workspace, belongs to the caller and no pointer is
+ *    kept after the call, except by work still in flight on `stream`.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every device call only enqueues work on it and returns without a device
+ *    synchronisation; results are ready when the stream has drained.
+ *  - Errors are returned as cb_status; nothing aborts or throws across the
+ *    ABI.  Argument and shape checks happen on the host before anything is
+ *    enqueued.  Device index arrays are not read on the host: out-of-range
+ *    entries are skipped by the kernels' bounds checks and make the results
+ *    unspecified, never an out-of-bounds access.  A failed HIP launch returns
+ *    CB_ERR_HIP and its code is kept per thread (cb_last_hip_error).
+ *  - Calls that share a workspace or a cache must not overlap in time.
+ */
+#ifndef CACHEBLEND_H
+#define CACHEBLEND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CB_OK = 0,
+  CB_ERR_ARG = 1,          /* null pointer, negative size, bad enum            */
+  CB_ERR_SHAPE = 2,        /* inconsistent geometry or head layout             */
+  CB_ERR_INDEX = 3,        /* reserved: index validation                       */
+  CB_ERR_WORKSPACE = 4,    /* workspace smaller than cb_workspace_size()       */
+  CB_ERR_UNSUPPORTED = 5,  /* shape the gfx950 kernels do not handle           */
+  CB_ERR_HIP = 6           /* a HIP runtime call or launch failed              */
+} cb_status;
+
+typedef enum { CB_F32 = 0, CB_BF16 = 1 } cb_dtype;
+
+/* Shape of one Llama-style decoder layer (no biases, RMSNorm, GQA, SwiGLU).
+ * Requirements: n_q_heads % n_kv_heads == 0; head_dim a multiple of 8.  bf16 needs
+ * head_dim in {64, 128}, n_q_heads / n_kv_heads in {1, 2, 4, 8} and d_model,
+ * ffn_dim multiples of 8.  fp32 needs head_dim <= 256. */
+typedef struct {
+  int32_t d_model;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn_dim;
+  float rope_theta;
+  float rms_eps;
+  int32_t dtype;           /* cb_dtype */
+} cb_layer_config;
+
+/* Device pointers to one layer's weights (layouts above).  attn_norm and
+ * mlp_norm are fp32 [d_model]. */
+typedef struct {
+  const void* attn_norm;
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_o;
+  const void* mlp_norm;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} cb_layer_weights;
+
+/* Device RoPE table: cos[p][hd/2], sin[p][hd/2] fp32 for p = 0 .. n_pos-1,
+ * as written by cb_rope_table(cfg, 0, n_pos, ...) and copied to the device. */
+typedef struct {
+  const float* cos;
+  const float* sin;
+  int32_t n_pos;
+} cb_rope_dev;
+
+/* ---------------------------------------------------------------------------
+ * Host helpers
+ * ------------------------------------------------------------------------- */
+
+/* RoPE table for positions pos_begin .. pos_begin+n_pos-1 into HOST buffers
+ * cos_out/sin_out [n_pos][head_dim/2] (CacheBlend section 4.3, footnote 3:
+ * the rotation matrix of angle m*theta).  theta_i = pow(rope_theta, -2i/hd)
+ * and angle = p * theta_i are evaluated in fp64 and cos/sin are rounded once
+ * to fp32 (round to nearest even).  CB_ERR_ARG on null or negative input. */
+cb_status cb_rope_table(const cb_layer_config* cfg, int32_t pos_begin, int32_t n_pos,
+                        float* cos_out, float* sin_out);
+
+/* Number of HKVD tokens for a recompute ratio r = r_e4 / 10000 over n_ctx
+ * context tokens (section 4.2: recomputing r% of the tokens): min(ceil(r *
+ * n_ctx), n_cand), in exact integer arithmetic.  -1 on negative input. */
+int32_t cb_num_selected(int32_t r_e4, int32_t n_ctx, int32_t n_cand);
+
+/* Gradual filtering schedule (section 4.3, Figure 9) into HOST k_out[n_layers]:
+ * layer 0 recomputes every candidate (k_out[0] = n_cand); layer l >= 1 keeps
+ * ceil(r_l * n_ctx) tokens with r_l falling linearly from r_first (l = 1) to
+ * r_last (l = n_layers-1); r_last_e4 == 0 keeps r_first on every layer.  k
+ * never grows from one layer to the next. */
+cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, int32_t r_last_e4,
+                             int32_t n_ctx, int32_t n_cand, int32_t* k_out);
+
+/* Bytes of device workspace needed by cb_blend_layer with up to m_max input
+ * rows and by cb_full_prefill_layer with T <= m_max rows, and by
+ * cb_select_hkvd with n <= m_max candidates.  0 on invalid cfg. */
+size_t cb_workspace_size(const cb_layer_config* cfg, int32_t T, int32_t m_max);
+
+const char* cb_status_string(cb_status s);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int32_t cb_last_hip_error(void);
+
+/* Kernel timing.  Between cb_profile_begin and cb_profile_end every kernel
+ * the library launches from this thread is bracketed by two hipEvents
+ * recorded on its stream (events are created on first use and reused; no
+ * device memory is allocated).  cb_profile_end waits for those events and
+ * writes one record per kernel name (up to max_out) to out (host); it returns
+ * the number of distinct names, or -1 if an event could not be read. */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;
+  double min_ms;
+  double max_ms;
+} cb_kernel_stat;
+
+cb_status cb_profile_begin(void);
+int32_t cb_profile_end(cb_kernel_stat* out, int32_t max_out);
+
+/* ---------------------------------------------------------------------------
+ * Device calls
+ * ------------------------------------------------------------------------- */
+
+/* RoPE position re-alignment of cached keys (section 4.3, footnote 3; the
+ * aifetchly guide: R(m + delta) = R(delta) R(m), values untouched).
+ * k_cache: device, n_layers buffers [T][n_kv][hd], buffer l at element offset
+ * l * layer_stride_elems; modified in place.  chunk_offsets: host int32
+ * [n_chunks+1], non-decreasing, chunk_offsets[0] = 0, chunk_offsets[n_chunks]
+ * = n_ctx <= T.  Every row of chunk c >= 1 is rotated once more by delta =
+ * chunk_offsets[c]; rows of chunk 0 and query rows are not touched.  The
+ * rotation is done in fp32 as two rounded products and one rounded sum per
+ * output, then stored in the cache dtype (round to nearest even).
+ * Needs rope->n_pos > chunk_offsets[n_chunks-1]; 1 <= n_chunks <= 256. */
+cb_status cb_rope_shift(const cb_layer_config* cfg, const cb_rope_dev* rope, void* k_cache,
+                        int64_t layer_stride_elems, int32_t n_layers, int32_t T,
+                        const int32_t* chunk_offsets, int32_t n_chunks, void* stream);
+
+/* HKVD selection (section 4.1 KV deviation, section 4.3 top tokens).
+ * n candidates, candidate i has token id cand_rows[i] (device int32 [n],
+ * strictly ascending; NULL means token id i).
+ * If k_new != NULL (device [n][n_kv][hd], cfg dtype): dev[i] = squared L2 norm
+ * over all KV heads of k_new[i] - k_ref[cand_rows[i]] (k_ref device [T][n_kv]
+ * [hd]), computed in fp32 from the stored values, is written to dev (device
+ * fp32 [n]).  If k_new == NULL, dev is an input.  The k largest deviations,
+ * ranked by (deviation descending, candidate index ascending), are written
+ * to sel_out (device int32 [k]) as token ids in ascending order.
+ * 0 <= k <= n; workspace >= cb_workspace_size(cfg, T, n). */
+cb_status cb_select_hkvd(const cb_layer_config* cfg, const void* k_new, const void* k_ref,
+                         int32_t T, const int32_t* cand_rows, int32_t n, int32_t k, float* dev,
+                         int32_t* sel_out, void* ws, size_t ws_bytes, void* stream);
+
+/* One layer of selective KV recompute (section 4.2, Figure 5b; HKVD
+ * selection of section 4.3).
+ *  k_cache, v_cache: device [T][n_kv][hd], this layer's cache with keys
+ *      already at their absolute positions (cb_rope_shift).  The new K/V of
+ *      every row of s_in are written in place; other rows are not touched.
+ *  s_in: device int32 [m_in], strictly ascending token ids, all >= first_
+ *      chunk_len; its last T - n_ctx entries are the query rows n_ctx..T-1.
+ *  hidden_in: device [*][d]; row in_rows[i] (device int32 [m_in]; NULL means
+ *      row i) is the layer input of token s_in[i].
+ *  k_out: how many candidates (s_in entries < n_ctx) to keep.  The kept set
+ *      s_out is the k_out candidates of largest K deviation (squared L2 of new
+ *      minus cached K over all KV heads, read before the cache row is
+ *      replaced), ranked by (deviation desc, token id asc), plus every query
+ *      row, in ascending token order.  If k_out >= the candidate count, s_out
+ *      = s_in.  m_out = min(k_out, m_in - (T - n_ctx)) + (T - n_ctx) is
+ *      written to *m_out_host (host, may be NULL) before the call returns.
+ *  Outputs (device): hidden_out [m_out][d] (the layer output of the kept
+ *      rows, in s_out order), dev_out fp32 [m_in] (NaN on query rows; may be
+ *      NULL), s_out int32 [m_out].  Attention of each kept row j is causal
+ *      over cache rows 0..j of the blended cache.
+ *  hidden_in must not alias hidden_out.
+ *  Workspace >= cb_workspace_size(cfg, T, m_in). */
+cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w,
+                         const cb_rope_dev* rope, void* k_cache, void* v_cache, int32_t T,
+                         int32_t n_ctx, int32_t first_chunk_len, const int32_t* s_in,
+                         int32_t m_in, const void* hidden_in, const int32_t* in_rows,
+                         int32_t k_out, void* hidden_out, float* dev_out, int32_t* s_out,
+                         int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream);
+
+/* The ordinary decoder layer over T rows at positions pos0 .. pos0+T-1 (the
+ * "full KV recompute" baseline of section 7 and the isolated precompute of a
+ * chunk at position 0).  hidden_in device [T][d]; k_out, v_out device
+ * [T][n_kv][hd] receive the layer's K (rotated) and V; hidden_out device
+ * [T][d].  Attention of row i is causal over rows 0..i.
+ * Workspace >= cb_workspace_size(cfg, T, T). */
+cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_layer_weights* w,
+                                const cb_rope_dev* rope, const void* hidden_in, int32_t T,
+                                int32_t pos0, void* k_out, void* v_out, void* hidden_out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CACHEBLEND_H */

@@ -1,0 +1,599 @@
+// C ABI of the fusor: argument checks, workspace layout and the launch
+// sequence of one layer on the caller's stream.
+//
+// cb_blend_layer follows CacheBlend (arXiv 2405.16444) section 4.2, Figure
+// 5b, with the HKVD selection of section 4.3:
+//   1. mask: gather the selected rows' inputs and apply the attention RMSNorm
+//   2. Q/K/V of those rows only; RoPE at their absolute positions; the K
+//      deviation against the cached row is summed before the new K/V replace
+//      the cached entries (expansion with the reused entries of other rows)
+//   3. keep the top-k rows by deviation plus the query rows
+//   4. attention of the kept rows over the blended cache
+//   5. output projection + residual, RMSNorm, SwiGLU MLP + residual
+// Every step is a kernel enqueued on the caller's stream; the host never
+// waits on the device.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cb_internal.h"
+
+namespace cb {
+
+// ---------------------------------------------------------------------------
+// per-thread state: last HIP error, optional kernel timing
+// ---------------------------------------------------------------------------
+namespace {
+
+thread_local int32_t t_last_hip = 0;
+
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+thread_local bool t_prof = false;
+thread_local std::vector<ProfRec> t_recs;
+thread_local std::vector<hipEvent_t> t_pool;
+
+hipEvent_t pool_get() {
+  if (!t_pool.empty()) {
+    hipEvent_t e = t_pool.back();
+    t_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+cb_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return CB_OK;
+  t_last_hip = (int32_t)e;
+  return CB_ERR_HIP;
+}
+
+}  // namespace
+
+LaunchScope::LaunchScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (!t_prof) return;
+  ProfRec r{name, pool_get(), pool_get()};
+  if (!r.a || !r.b) return;
+  (void)hipEventRecord(r.a, s);
+  t_recs.push_back(r);
+  slot = (int)t_recs.size() - 1;
+}
+
+LaunchScope::~LaunchScope() {
+  if (slot >= 0) (void)hipEventRecord(t_recs[slot].b, stream);
+}
+
+// ---------------------------------------------------------------------------
+// validation and workspace
+// ---------------------------------------------------------------------------
+namespace {
+
+cb_status check_cfg(const cb_layer_config* c) {
+  if (!c) return CB_ERR_ARG;
+  if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->ffn_dim <= 0)
+    return CB_ERR_ARG;
+  if (c->dtype != CB_F32 && c->dtype != CB_BF16) return CB_ERR_ARG;
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return CB_ERR_ARG;
+  if (c->n_q_heads % c->n_kv_heads) return CB_ERR_SHAPE;
+  if (c->head_dim % 8 || c->d_model % 8 || c->ffn_dim % 8) return CB_ERR_SHAPE;
+  if (c->dtype == CB_BF16) {
+    if (c->head_dim != 64 && c->head_dim != 128) return CB_ERR_UNSUPPORTED;
+    const int g = c->n_q_heads / c->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return CB_ERR_UNSUPPORTED;
+  } else if (c->head_dim > 256) {
+    return CB_ERR_UNSUPPORTED;
+  }
+  return CB_OK;
+}
+
+constexpr int kF32MaxT = 8192;  // fp32 attention keeps a row's scores in LDS
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Dims {
+  int d, q_dim, kv_dim, hd, F, b, bn;
+  explicit Dims(const cb_layer_config& c)
+      : d(c.d_model), q_dim(c.n_q_heads * c.head_dim), kv_dim(c.n_kv_heads * c.head_dim), hd(c.head_dim),
+        F(c.ffn_dim), b(c.dtype == CB_BF16 ? 2 : 4), bn(gemm_bn(c.dtype)) {}
+  int n_qkv() const { return q_dim + 2 * kv_dim; }
+  int k_tile0() const { return q_dim / bn; }
+  int n_k_tiles() const { return (q_dim + kv_dim - 1) / bn - k_tile0() + 1; }
+};
+
+struct Ws {
+  size_t xn, q, devp, dev, sel, o, h, hn, u, part, scratch, total;
+};
+
+BOperand b_single(const void* p, int n) {
+  BOperand B{};
+  B.mode = 0;
+  B.p0 = B.p1 = B.p2 = p;
+  B.n1 = B.n2 = n;
+  B.n_feat = n;
+  return B;
+}
+
+size_t part_floats(int dtype, const Dims& D, int m) {
+  // largest split-K partial buffer over the four projections
+  size_t best = 0;
+  auto consider = [&](const BOperand& B, int N, int K) {
+    const int nt = gemm_n_tiles(dtype, B, N);
+    const int sp = gemm_splits(dtype, nt, K);
+    if (sp > 1) best = std::max(best, (size_t)sp * m * nt * D.bn);
+  };
+  BOperand qkv = b_single(nullptr, D.n_qkv());
+  consider(qkv, D.n_qkv(), D.d);
+  consider(b_single(nullptr, D.d), D.d, D.q_dim);
+  BOperand gu{};
+  gu.mode = 1;
+  gu.n_feat = D.F;
+  consider(gu, 0, D.d);
+  consider(b_single(nullptr, D.d), D.d, D.F);
+  return best;
+}
+
+Ws layout(const cb_layer_config& c, int m) {
+  const Dims D(c);
+  Ws w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t M = (size_t)std::max(m, 1);
+  w.xn = take(M * D.d * D.b);
+  w.q = take(M * D.q_dim * D.b);
+  w.devp = take((size_t)D.n_k_tiles() * M * 4);
+  w.dev = take(M * 4);
+  w.sel = take(M * 4);
+  w.o = take(M * D.q_dim * D.b);
+  w.h = take(M * D.d * 4);
+  w.hn = take(M * D.d * D.b);
+  w.u = take(M * D.F * D.b);
+  w.part = take(part_floats(c.dtype, D, (int)M) * 4);
+  w.scratch = take(256);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+cb_status check_rope(const cb_rope_dev* r, int need) {
+  if (!r || !r->cos || !r->sin) return CB_ERR_ARG;
+  if (r->n_pos < need) return CB_ERR_SHAPE;
+  return CB_OK;
+}
+
+cb_status check_weights(const cb_layer_weights* w) {
+  if (!w) return CB_ERR_ARG;
+  const void* p[9] = {w->attn_norm, w->w_q, w->w_k, w->w_v, w->w_o, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+  for (const void* x : p)
+    if (!x || !aligned16(x)) return CB_ERR_ARG;
+  return CB_OK;
+}
+
+// The part of a layer after attention: O projection + residual, RMSNorm,
+// SwiGLU MLP, down projection + residual.  resid rows: map(i) = m2[m1[i]].
+cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const Ws& L, void* ws, int m_out,
+                     const void* hidden_in, int n_resid, const int* m1, const int* m2, void* hidden_out,
+                     hipStream_t s) {
+  const Dims D(c);
+  const int dt = c.dtype;
+  // O projection + residual -> h (fp32)
+  GemmArgs g{};
+  g.A = at<void>(ws, L.o);
+  g.M = m_out;
+  g.N = D.d;
+  g.K = D.q_dim;
+  g.B = b_single(w.w_o, D.d);
+  g.epi.kind = EPI_RESID;
+  g.epi.resid = hidden_in;
+  g.epi.resid_f32 = 0;
+  g.epi.rmap1 = m1;
+  g.epi.rmap2 = m2;
+  g.epi.T = n_resid;
+  g.epi.out = at<void>(ws, L.h);
+  g.epi.out_f32 = 1;
+  g.epi.ld_out = D.d;
+  g.splits = gemm_splits(dt, gemm_n_tiles(dt, g.B, g.N), g.K);
+  g.part = at<float>(ws, L.part);
+  cb_status st = hip_status(launch_gemm(dt, g, s));
+  if (st) return st;
+  // RMSNorm(h) -> hn
+  st = hip_status(launch_rmsnorm(dt, true, at<void>(ws, L.h), m_out, nullptr, nullptr, (const float*)w.mlp_norm,
+                                 at<void>(ws, L.hn), m_out, D.d, c.rms_eps, s));
+  if (st) return st;
+  // gate/up + SwiGLU -> u
+  GemmArgs gu{};
+  gu.A = at<void>(ws, L.hn);
+  gu.M = m_out;
+  gu.K = D.d;
+  gu.B.mode = 1;
+  gu.B.p0 = w.w_gate;
+  gu.B.p1 = w.w_up;
+  gu.B.p2 = w.w_up;
+  gu.B.n_feat = D.F;
+  gu.epi.kind = EPI_SWIGLU;
+  gu.epi.out = at<void>(ws, L.u);
+  gu.epi.ld_out = D.F;
+  gu.splits = gemm_splits(dt, gemm_n_tiles(dt, gu.B, 0), gu.K);
+  gu.part = at<float>(ws, L.part);
+  st = hip_status(launch_gemm(dt, gu, s));
+  if (st) return st;
+  // down projection + residual (h) -> hidden_out
+  GemmArgs gd{};
+  gd.A = at<void>(ws, L.u);
+  gd.M = m_out;
+  gd.N = D.d;
+  gd.K = D.F;
+  gd.B = b_single(w.w_down, D.d);
+  gd.epi.kind = EPI_RESID;
+  gd.epi.resid = at<void>(ws, L.h);
+  gd.epi.resid_f32 = 1;
+  gd.epi.T = m_out;
+  gd.epi.out = hidden_out;
+  gd.epi.out_f32 = dt == CB_F32;
+  gd.epi.ld_out = D.d;
+  gd.splits = gemm_splits(dt, gemm_n_tiles(dt, gd.B, gd.N), gd.K);
+  gd.part = at<float>(ws, L.part);
+  return hip_status(launch_gemm(dt, gd, s));
+}
+
+// Fill the QKV projection arguments.
+GemmArgs qkv_args(const cb_layer_config& c, const cb_layer_weights& w, const cb_rope_dev& rope, const Ws& L,
+                  void* ws, int M) {
+  const Dims D(c);
+  GemmArgs g{};
+  g.A = at<void>(ws, L.xn);
+  g.M = M;
+  g.N = D.n_qkv();
+  g.K = D.d;
+  g.B.mode = 0;
+  g.B.p0 = w.w_q;
+  g.B.p1 = w.w_k;
+  g.B.p2 = w.w_v;
+  g.B.n1 = D.q_dim;
+  g.B.n2 = D.q_dim + D.kv_dim;
+  g.B.n_feat = g.N;
+  g.epi.kind = EPI_QKV;
+  g.epi.q_dim = D.q_dim;
+  g.epi.kv_dim = D.kv_dim;
+  g.epi.hd = D.hd;
+  g.epi.cos = rope.cos;
+  g.epi.sin = rope.sin;
+  g.epi.q_out = at<void>(ws, L.q);
+  g.epi.k_tile0 = D.k_tile0();
+  g.splits = gemm_splits(c.dtype, gemm_n_tiles(c.dtype, g.B, g.N), g.K);
+  g.part = at<float>(ws, L.part);
+  return g;
+}
+
+}  // namespace
+}  // namespace cb
+
+using namespace cb;
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+
+extern "C" cb_status cb_rope_table(const cb_layer_config* cfg, int32_t pos_begin, int32_t n_pos, float* cos_out,
+                                   float* sin_out) {
+  if (!cfg || !cos_out || !sin_out || pos_begin < 0 || n_pos < 0) return CB_ERR_ARG;
+  if (cfg->head_dim <= 0 || cfg->head_dim % 2 || !(cfg->rope_theta > 0.f)) return CB_ERR_ARG;
+  const int half = cfg->head_dim / 2;
+  std::vector<double> inv(half);
+  for (int i = 0; i < half; ++i) inv[i] = pow((double)cfg->rope_theta, -2.0 * i / cfg->head_dim);
+  for (int p = 0; p < n_pos; ++p) {
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)(pos_begin + p) * inv[i];
+      cos_out[(size_t)p * half + i] = (float)cos(ang);
+      sin_out[(size_t)p * half + i] = (float)sin(ang);
+    }
+  }
+  return CB_OK;
+}
+
+extern "C" int32_t cb_num_selected(int32_t r_e4, int32_t n_ctx, int32_t n_cand) {
+  if (r_e4 < 0 || n_ctx < 0 || n_cand < 0) return -1;
+  const int64_t num = (int64_t)r_e4 * n_ctx;
+  const int64_t k = (num + 9999) / 10000;  // ceil for num >= 0
+  return (int32_t)std::min<int64_t>(k, n_cand);
+}
+
+extern "C" cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, int32_t r_last_e4, int32_t n_ctx,
+                                        int32_t n_cand, int32_t* k_out) {
+  if (n_layers <= 0 || r_first_e4 < 0 || r_last_e4 < 0 || n_ctx < 0 || n_cand < 0 || !k_out) return CB_ERR_ARG;
+  k_out[0] = n_cand;
+  for (int l = 1; l < n_layers; ++l) {
+    // r_l = r_first - (r_first - r_last) * (l-1)/(L-2), in units of 1e-4;
+    // k = ceil(r_l * n_ctx / 1e4) computed exactly over the common denominator
+    int64_t k;
+    if (r_last_e4 == 0 || n_layers <= 2) {
+      k = ((int64_t)r_first_e4 * n_ctx + 9999) / 10000;
+    } else {
+      const int64_t den = (int64_t)(n_layers - 2);
+      const int64_t r_num = (int64_t)r_first_e4 * den - (int64_t)(r_first_e4 - r_last_e4) * (l - 1);
+      const int64_t num = r_num * n_ctx;            // r_l * n_ctx * 1e4 * den
+      const int64_t q = 10000 * den;
+      k = num >= 0 ? (num + q - 1) / q : -((-num) / q);
+    }
+    k = std::min<int64_t>(k, n_cand);
+    k = std::min<int64_t>(k, k_out[l - 1]);
+    k_out[l] = (int32_t)std::max<int64_t>(k, 0);
+  }
+  return CB_OK;
+}
+
+extern "C" size_t cb_workspace_size(const cb_layer_config* cfg, int32_t T, int32_t m_max) {
+  if (check_cfg(cfg) != CB_OK || T < 0 || m_max < 0) return 0;
+  return layout(*cfg, std::max(T, m_max)).total;
+}
+
+extern "C" const char* cb_status_string(cb_status s) {
+  switch (s) {
+    case CB_OK: return "ok";
+    case CB_ERR_ARG: return "invalid argument";
+    case CB_ERR_SHAPE: return "inconsistent shape";
+    case CB_ERR_INDEX: return "index out of range";
+    case CB_ERR_WORKSPACE: return "workspace too small";
+    case CB_ERR_UNSUPPORTED: return "unsupported shape for the gfx950 kernels";
+    case CB_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" int32_t cb_last_hip_error(void) { return t_last_hip; }
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+
+extern "C" cb_status cb_profile_begin(void) {
+  t_prof = true;
+  return CB_OK;
+}
+
+extern "C" int32_t cb_profile_end(cb_kernel_stat* out, int32_t max_out) {
+  t_prof = false;
+  struct Acc {
+    std::string name;
+    int n;
+    double tot, mn, mx;
+  };
+  std::vector<Acc> acc;
+  int32_t bad = 0;
+  for (auto& r : t_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      bad = 1;
+    } else {
+      auto it = std::find_if(acc.begin(), acc.end(), [&](const Acc& a) { return a.name == r.name; });
+      if (it == acc.end()) acc.push_back(Acc{r.name, 1, ms, ms, ms});
+      else {
+        it->n += 1;
+        it->tot += ms;
+        it->mn = std::min(it->mn, (double)ms);
+        it->mx = std::max(it->mx, (double)ms);
+      }
+    }
+    t_pool.push_back(r.a);
+    t_pool.push_back(r.b);
+  }
+  t_recs.clear();
+  if (bad) return -1;
+  const int n = (int)acc.size();
+  for (int i = 0; i < n && i < max_out && out; ++i) {
+    memset(&out[i], 0, sizeof(out[i]));
+    strncpy(out[i].name, acc[i].name.c_str(), sizeof(out[i].name) - 1);
+    out[i].launches = acc[i].n;
+    out[i].total_ms = acc[i].tot;
+    out[i].min_ms = acc[i].mn;
+    out[i].max_ms = acc[i].mx;
+  }
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+// device calls
+// ---------------------------------------------------------------------------
+
+extern "C" cb_status cb_rope_shift(const cb_layer_config* cfg, const cb_rope_dev* rope, void* k_cache,
+                                   int64_t layer_stride_elems, int32_t n_layers, int32_t T,
+                                   const int32_t* chunk_offsets, int32_t n_chunks, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!k_cache || !chunk_offsets || n_layers < 0 || T < 0 || n_chunks < 1 || !aligned16(k_cache))
+    return CB_ERR_ARG;
+  if (n_chunks > 256) return CB_ERR_UNSUPPORTED;
+  if (chunk_offsets[0] != 0) return CB_ERR_SHAPE;
+  for (int c = 0; c < n_chunks; ++c)
+    if (chunk_offsets[c + 1] < chunk_offsets[c]) return CB_ERR_SHAPE;
+  if (chunk_offsets[n_chunks] > T) return CB_ERR_SHAPE;
+  const Dims D(*cfg);
+  if (n_layers > 1 && layer_stride_elems < (int64_t)T * D.kv_dim) return CB_ERR_SHAPE;
+  if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
+  st = check_rope(rope, n_chunks > 1 ? chunk_offsets[n_chunks - 1] + 1 : 0);
+  if (st) return st;
+  RopeShiftArgs a{};
+  a.k_cache = k_cache;
+  a.layer_stride = layer_stride_elems;
+  a.n_layers = n_layers;
+  a.T = T;
+  a.kv_dim = D.kv_dim;
+  a.hd = D.hd;
+  a.cos = rope->cos;
+  a.sin = rope->sin;
+  a.offsets = chunk_offsets;
+  a.n_chunks = n_chunks;
+  return hip_status(launch_rope_shift(cfg->dtype, a, (hipStream_t)stream));
+}
+
+extern "C" cb_status cb_select_hkvd(const cb_layer_config* cfg, const void* k_new, const void* k_ref, int32_t T,
+                                    const int32_t* cand_rows, int32_t n, int32_t k, float* dev, int32_t* sel_out,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (n < 0 || k < 0 || k > n || !dev || (k > 0 && !sel_out) || T < 0) return CB_ERR_ARG;
+  if (k_new && (!k_ref || !aligned16(k_new) || !aligned16(k_ref))) return CB_ERR_ARG;
+  if (!ws) return CB_ERR_ARG;
+  if (ws_bytes < cb_workspace_size(cfg, T, n)) return CB_ERR_WORKSPACE;
+  if (n == 0) return CB_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const Dims D(*cfg);
+  if (k_new) {
+    st = hip_status(launch_kdev(cfg->dtype, k_new, k_ref, cand_rows, n, D.kv_dim, T, dev, s));
+    if (st) return st;
+  }
+  SelectArgs a{};
+  a.dev = dev;
+  a.n_cand = n;
+  a.m_in = n;
+  a.k = k;
+  a.ids_in = cand_rows;
+  a.ids_out = sel_out;
+  return hip_status(launch_select(a, s));
+}
+
+extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
+                                    void* k_cache, void* v_cache, int32_t T, int32_t n_ctx, int32_t first_chunk_len,
+                                    const int32_t* s_in, int32_t m_in, const void* hidden_in,
+                                    const int32_t* in_rows, int32_t k_out, void* hidden_out, float* dev_out,
+                                    int32_t* s_out, int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  st = check_weights(w);
+  if (st) return st;
+  if (!k_cache || !v_cache || !s_in || !hidden_in || !hidden_out || !s_out || !ws) return CB_ERR_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(hidden_in) || !aligned16(hidden_out) ||
+      !aligned16(ws))
+    return CB_ERR_ARG;
+  if (T <= 0 || n_ctx < 0 || first_chunk_len < 0 || m_in < 0 || k_out < 0) return CB_ERR_ARG;
+  if (n_ctx > T || first_chunk_len > n_ctx) return CB_ERR_SHAPE;
+  const int n_query = T - n_ctx;
+  const int n_cand = m_in - n_query;
+  if (n_cand < 0 || n_cand > n_ctx - first_chunk_len) return CB_ERR_SHAPE;
+  if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
+  st = check_rope(rope, T);
+  if (st) return st;
+  if (ws_bytes < cb_workspace_size(cfg, T, m_in)) return CB_ERR_WORKSPACE;
+  const int m_out = std::min(k_out, n_cand) + n_query;
+  if (m_out_host) *m_out_host = m_out;
+  if (m_in == 0) return CB_OK;
+
+  const Dims D(*cfg);
+  const Ws L = layout(*cfg, m_in);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = cfg->dtype;
+  const int n_src = in_rows ? T : m_in;
+
+  // 1. gather + attention RMSNorm
+  st = hip_status(launch_rmsnorm(dt, false, hidden_in, n_src, nullptr, in_rows, (const float*)w->attn_norm,
+                                 at<void>(ws, L.xn), m_in, D.d, cfg->rms_eps, s));
+  if (st) return st;
+  // 2. QKV + RoPE + deviation + K/V scatter
+  GemmArgs g = qkv_args(*cfg, *w, *rope, L, ws, m_in);
+  g.epi.rows = s_in;
+  g.epi.pos0 = 0;
+  g.epi.dev_lo = first_chunk_len;
+  g.epi.dev_hi = n_ctx;
+  g.epi.k_cache = k_cache;
+  g.epi.v_cache = v_cache;
+  g.epi.T = T;
+  g.epi.dev_part = at<float>(ws, L.devp);
+  st = hip_status(launch_gemm(dt, g, s));
+  if (st) return st;
+  // 3. deviation sums + top-k + query rows
+  SelectArgs sa{};
+  sa.dev_part = at<float>(ws, L.devp);
+  sa.n_parts = D.n_k_tiles();
+  sa.ld_part = m_in;
+  sa.dev = dev_out ? dev_out : at<float>(ws, L.dev);
+  sa.n_cand = n_cand;
+  sa.m_in = m_in;
+  sa.k = k_out;
+  sa.ids_in = s_in;
+  sa.sel = at<int>(ws, L.sel);
+  sa.ids_out = s_out;
+  st = hip_status(launch_select(sa, s));
+  if (st) return st;
+  // 4. attention of the kept rows over the blended cache
+  AttnArgs aa{};
+  aa.Q = at<void>(ws, L.q);
+  aa.qmap = at<int>(ws, L.sel);
+  aa.qpos = s_out;
+  aa.K = k_cache;
+  aa.V = v_cache;
+  aa.O = at<void>(ws, L.o);
+  aa.m = m_out;
+  aa.T = T;
+  aa.n_q = cfg->n_q_heads;
+  aa.n_kv = cfg->n_kv_heads;
+  aa.hd = D.hd;
+  st = hip_status(launch_attention(dt, aa, s));
+  if (st) return st;
+  // 5. O projection, MLP
+  return layer_tail(*cfg, *w, L, ws, m_out, hidden_in, n_src, at<int>(ws, L.sel), in_rows, hidden_out, s);
+}
+
+extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_layer_weights* w,
+                                           const cb_rope_dev* rope, const void* hidden_in, int32_t T, int32_t pos0,
+                                           void* k_out, void* v_out, void* hidden_out, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  st = check_weights(w);
+  if (st) return st;
+  if (!hidden_in || !k_out || !v_out || !hidden_out || !ws) return CB_ERR_ARG;
+  if (!aligned16(hidden_in) || !aligned16(k_out) || !aligned16(v_out) || !aligned16(hidden_out) || !aligned16(ws))
+    return CB_ERR_ARG;
+  if (T < 0 || pos0 < 0) return CB_ERR_ARG;
+  if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
+  st = check_rope(rope, pos0 + T);
+  if (st) return st;
+  if (ws_bytes < cb_workspace_size(cfg, T, T)) return CB_ERR_WORKSPACE;
+  if (T == 0) return CB_OK;
+  const Dims D(*cfg);
+  const Ws L = layout(*cfg, T);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = cfg->dtype;
+  st = hip_status(launch_rmsnorm(dt, false, hidden_in, T, nullptr, nullptr, (const float*)w->attn_norm,
+                                 at<void>(ws, L.xn), T, D.d, cfg->rms_eps, s));
+  if (st) return st;
+  GemmArgs g = qkv_args(*cfg, *w, *rope, L, ws, T);
+  g.epi.rows = nullptr;
+  g.epi.pos0 = pos0;
+  g.epi.k_cache = k_out;
+  g.epi.v_cache = v_out;
+  g.epi.T = T;
+  g.epi.dev_part = nullptr;
+  st = hip_status(launch_gemm(dt, g, s));
+  if (st) return st;
+  AttnArgs aa{};
+  aa.Q = at<void>(ws, L.q);
+  aa.K = k_out;
+  aa.V = v_out;
+  aa.O = at<void>(ws, L.o);
+  aa.m = T;
+  aa.T = T;
+  aa.n_q = cfg->n_q_heads;
+  aa.n_kv = cfg->n_kv_heads;
+  aa.hd = D.hd;
+  st = hip_status(launch_attention(dt, aa, s));
+  if (st) return st;
+  return layer_tail(*cfg, *w, L, ws, T, hidden_in, T, nullptr, nullptr, hidden_out, s);
+}

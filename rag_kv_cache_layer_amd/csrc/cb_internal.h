@@ -1,0 +1,195 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cacheblend.h"
+
+namespace cb {
+
+typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float rnd(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+  static __device__ __forceinline__ float rnd(float v) { return bf2f(f2bf(v)); }
+};
+
+// Load / store 8 consecutive elements (16 B for bf16, 32 B for fp32).
+__device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float v[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f2bf(v[2 * j]) | ((uint32_t)f2bf(v[2 * j + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Composite row map: r = i; r = m1[r] if m1; r = m2[r] if m2.
+__device__ __forceinline__ int map_row(int i, const int* m1, const int* m2) {
+  int r = m1 ? m1[i] : i;
+  return m2 ? m2[r] : r;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing hooks (host side).  When profiling is on, every launch below
+// is bracketed by hipEvents recorded on its stream.
+// ---------------------------------------------------------------------------
+struct LaunchScope {
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  int slot;
+  hipStream_t stream;
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (host).  All return hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+
+struct RopeShiftArgs {
+  void* k_cache;
+  int64_t layer_stride;
+  int n_layers;
+  int T;
+  int kv_dim;     // n_kv * hd
+  int hd;
+  const float* cos;
+  const float* sin;
+  const int32_t* offsets;  // host, n_chunks + 1
+  int n_chunks;
+};
+hipError_t launch_rope_shift(int dtype, const RopeShiftArgs& a, hipStream_t s);
+
+// RMSNorm of gathered rows: out[i] = x[map(i)] / sqrt(mean(x^2) + eps) * g.
+// x_f32 selects an fp32 input regardless of the storage dtype.
+hipError_t launch_rmsnorm(int dtype, bool x_f32, const void* x, int n_src, const int* m1, const int* m2,
+                          const float* g, void* out, int rows, int d, float eps, hipStream_t s);
+
+// Deviation of candidate rows, then top-k.  See select.hip.
+struct SelectArgs {
+  const float* dev_part;   // [n_parts][ld_part] partial sums, or NULL
+  int n_parts;
+  int ld_part;
+  float* dev;              // [m_in] full deviation (written from the partials, or read)
+  int n_cand;              // candidates are entries 0 .. n_cand-1
+  int m_in;                // entries n_cand .. m_in-1 are always kept (query rows)
+  int k;                   // candidates to keep
+  const int* ids_in;       // token ids of the entries, NULL = identity
+  int* sel;                // [m_out] kept entry positions, ascending (may be NULL)
+  int* ids_out;            // [m_out] kept token ids (may be NULL)
+  uint32_t* scratch;       // >= 16 words
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+// dev[i] = sum over kv_dim of (k_new[i] - k_ref[rows[i]])^2.
+hipError_t launch_kdev(int dtype, const void* k_new, const void* k_ref, const int* rows, int n,
+                       int kv_dim, int T, float* dev, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// GEMM: C[M][N] = A[M][K] * B[N][K]^T with fused epilogues.
+// ---------------------------------------------------------------------------
+struct BOperand {
+  // mode 0: rows [0, n1) from p0, [n1, n2) from p1, [n2, N) from p2.
+  // mode 1 (gated pair): output tile columns [0, BN/2) are rows of p0
+  //   (features tile*BN/2 + j) and [BN/2, BN) the same rows of p1; n_feat
+  //   features in total.
+  int mode;
+  const void* p0;
+  const void* p1;
+  const void* p2;
+  int n1, n2;
+  int n_feat;
+};
+
+enum EpiKind { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_STORE = 3 };
+
+struct EpiParams {
+  int kind;
+  // QKV
+  int q_dim, kv_dim, hd;
+  const int* rows;        // cache row of GEMM row i (NULL = i)
+  int pos0;               // RoPE position = cache row + pos0
+  int dev_lo, dev_hi;     // deviation for cache rows in [dev_lo, dev_hi)
+  const float* cos;
+  const float* sin;
+  void* q_out;            // [M][q_dim]
+  void* k_cache;          // [T][kv_dim]
+  void* v_cache;
+  int T;
+  float* dev_part;        // [n_k_tiles][M] or NULL
+  int k_tile0;            // first N tile intersecting the K columns
+  // RESID: out[i][c] = resid[map(i)][c] + acc
+  const void* resid;
+  int resid_f32;
+  const int* rmap1;
+  const int* rmap2;
+  void* out;
+  int out_f32;
+  int ld_out;
+};
+
+struct GemmArgs {
+  const void* A;
+  int M, N, K;
+  BOperand B;
+  EpiParams epi;
+  int splits;             // split-K factor (bf16 only)
+  float* part;            // [splits][M][n_tiles*BN] fp32 partials when splits > 1
+};
+
+int gemm_bn(int dtype);                               // N tile width
+int gemm_splits(int dtype, int N_tiles, int K);       // split-K choice (independent of M)
+int gemm_n_tiles(int dtype, const BOperand& B, int N);
+hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Attention of selected rows over the cache.
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  const void* Q;          // [*][n_q*hd]; row qmap[i] (NULL = i) holds query i
+  const int* qmap;
+  const int* qpos;        // query i attends cache rows 0 .. qpos[i] (NULL = i)
+  const void* K;          // [T][n_kv*hd]
+  const void* V;
+  void* O;                // [m][n_q*hd]
+  int m, T, n_q, n_kv, hd;
+};
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
+
+}  // namespace cb

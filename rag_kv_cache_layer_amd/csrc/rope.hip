@@ -1,0 +1,85 @@
+// RoPE position re-alignment of cached keys, in place, over many layers.
+//
+// CacheBlend (arXiv 2405.16444) section 4.3, footnote 3: a chunk's keys were
+// rotated at the positions the chunk had when it was prefilled alone; after
+// it is placed at offset delta, one more rotation by delta*theta_i per pair
+// moves every key to its absolute position (the aifetchly guide, "RoPE Delta
+// Positional Realignment": R(m + delta) = R(delta) R(m)); values stay as they
+// are.
+//
+// The kernel is HBM-bound: every shifted element is read once and written
+// once.  One thread moves 8 consecutive elements (4 pairs) of one key row:
+// 16 B loads and stores for bf16, coalesced along the row; the cos/sin rows of
+// the few distinct deltas stay in L2.
+#include "cb_internal.h"
+
+namespace cb {
+
+namespace {
+
+constexpr int kMaxChunks = 256;
+
+struct ChunkOffsets {
+  int32_t o[kMaxChunks + 1];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int64_t lstride, int kv_dim,
+                                                         int hd, int row0, int n_rows, int units_per_row,
+                                                         int64_t total, const float* __restrict__ cosp,
+                                                         const float* __restrict__ sinp, ChunkOffsets offs,
+                                                         int n_chunks) {
+  int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= total) return;
+  int cu = (int)(u % units_per_row);
+  int64_t rr = u / units_per_row;
+  int r = row0 + (int)(rr % n_rows);
+  int l = (int)(rr / n_rows);
+  // chunk of row r: the largest c in [1, n_chunks-1] with o[c] <= r
+  int lo = 1, hi = n_chunks - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (offs.o[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int delta = offs.o[lo];
+  T* p = k + (int64_t)l * lstride + (int64_t)r * kv_dim + cu * 8;
+  const int e = (cu * 8) % hd;
+  const float* cs = cosp + (int64_t)delta * (hd / 2) + e / 2;
+  const float* sn = sinp + (int64_t)delta * (hd / 2) + e / 2;
+  float v[8], o[8];
+  load8(p, v);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = v[2 * j], b = v[2 * j + 1], c = cs[j], s = sn[j];
+    // two rounded products and one rounded sum per output, no fused multiply-add
+    o[2 * j] = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
+    o[2 * j + 1] = __fadd_rn(__fmul_rn(a, s), __fmul_rn(b, c));
+  }
+  store8(p, o);
+}
+
+}  // namespace
+
+hipError_t launch_rope_shift(int dtype, const RopeShiftArgs& a, hipStream_t s) {
+  if (a.n_chunks < 2 || a.n_layers <= 0) return hipSuccess;
+  const int row0 = a.offsets[1];
+  const int n_rows = a.offsets[a.n_chunks] - row0;
+  if (n_rows <= 0) return hipSuccess;
+  ChunkOffsets offs;
+  for (int c = 0; c <= a.n_chunks; ++c) offs.o[c] = a.offsets[c];
+  const int upr = a.kv_dim / 8;
+  const int64_t total = (int64_t)a.n_layers * n_rows * upr;
+  const int64_t blocks = (total + 255) / 256;
+  LaunchScope ls("rope_shift", s);
+  if (dtype == CB_BF16)
+    rope_shift_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        (bf16_t*)a.k_cache, a.layer_stride, a.kv_dim, a.hd, row0, n_rows, upr, total, a.cos, a.sin, offs,
+        a.n_chunks);
+  else
+    rope_shift_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        (float*)a.k_cache, a.layer_stride, a.kv_dim, a.hd, row0, n_rows, upr, total, a.cos, a.sin, offs,
+        a.n_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace cb

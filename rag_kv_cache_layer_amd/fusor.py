@@ -1,0 +1,297 @@
+"""Python binding of libcacheblend.so (the CacheBlend fusor for gfx950).
+
+Argument marshalling only: every step of the fusor runs in the library's HIP
+kernels.  torch is used for device memory and streams.  The function names
+and argument orders are those of ``include/cacheblend.h``; tensors are passed
+as device pointers after a shape / dtype / device check.
+
+The library must have been built (``python -m rag_kv_cache_layer_amd.build``
+or ``__graft_entry__.build()``); importing this module never compiles, and a
+missing library is an error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcacheblend.so")
+
+CB_F32, CB_BF16 = 0, 1
+_STATUS = {0: "CB_OK", 1: "CB_ERR_ARG", 2: "CB_ERR_SHAPE", 3: "CB_ERR_INDEX", 4: "CB_ERR_WORKSPACE",
+           5: "CB_ERR_UNSUPPORTED", 6: "CB_ERR_HIP"}
+
+
+class CacheBlendError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{where}: {_STATUS.get(status, status)}"
+        if status == 6:
+            msg += f" (hipError {hip_error})"
+        super().__init__(msg)
+
+
+class LayerConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn_dim", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up", "w_down")]
+
+
+class RopeDev(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32)]
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double),
+                ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32P, I32P = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, \
+        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)
+    CFG, W, R = ctypes.POINTER(LayerConfig), ctypes.POINTER(LayerWeights), ctypes.POINTER(RopeDev)
+    sig = {
+        "cb_rope_table": (I32, [CFG, I32, I32, F32P, F32P]),
+        "cb_num_selected": (I32, [I32, I32, I32]),
+        "cb_filter_schedule": (I32, [I32, I32, I32, I32, I32, I32P]),
+        "cb_workspace_size": (SZ, [CFG, I32, I32]),
+        "cb_status_string": (ctypes.c_char_p, [I32]),
+        "cb_last_hip_error": (I32, []),
+        "cb_profile_begin": (I32, []),
+        "cb_profile_end": (I32, [ctypes.POINTER(KernelStat), I32]),
+        "cb_rope_shift": (I32, [CFG, R, P, I64, I32, I32, I32P, I32, P]),
+        "cb_select_hkvd": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, SZ, P]),
+        "cb_blend_layer": (I32, [CFG, W, R, P, P, I32, I32, I32, P, I32, P, P, I32, P, P, P, I32P, P, SZ, P]),
+        "cb_full_prefill_layer": (I32, [CFG, W, R, P, I32, I32, P, P, P, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise CacheBlendError(status, where, lib().cb_last_hip_error())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def make_config(d_model: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn_dim: int,
+                rope_theta: float, rms_eps: float, dtype: str) -> LayerConfig:
+    return LayerConfig(int(d_model), int(n_q_heads), int(n_kv_heads), int(head_dim), int(ffn_dim),
+                       float(rope_theta), float(rms_eps), CB_BF16 if dtype == "bf16" else CB_F32)
+
+
+def config_of(p) -> LayerConfig:
+    """LayerConfig from an object with the preset fields (d_model, n_q_heads, ...)."""
+    return make_config(p.d_model, p.n_q_heads, p.n_kv_heads, p.head_dim, p.ffn_dim, p.rope_theta, p.rms_eps,
+                       p.dtype)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype(cfg: LayerConfig):
+    torch = _torch()
+    return torch.bfloat16 if cfg.dtype == CB_BF16 else torch.float32
+
+
+def _dptr(t, name: str, dtype=None, numel: Optional[int] = None):
+    """Device pointer of a contiguous CUDA/HIP tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# host helpers (no device needed)
+# ---------------------------------------------------------------------------
+
+def rope_table(cfg: LayerConfig, pos_begin: int, n_pos: int):
+    """(cos, sin) fp32 [n_pos][hd/2] from cb_rope_table."""
+    half = cfg.head_dim // 2
+    cos = np.empty((n_pos, half), dtype=np.float32)
+    sin = np.empty((n_pos, half), dtype=np.float32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    _check(lib().cb_rope_table(ctypes.byref(cfg), pos_begin, n_pos, cos.ctypes.data_as(fp), sin.ctypes.data_as(fp)),
+           "cb_rope_table")
+    return cos, sin
+
+
+def num_selected(r_e4: int, n_ctx: int, n_cand: int) -> int:
+    return int(lib().cb_num_selected(r_e4, n_ctx, n_cand))
+
+
+def filter_schedule(n_layers: int, r_first_e4: int, r_last_e4: int, n_ctx: int, n_cand: int):
+    out = (ctypes.c_int32 * n_layers)()
+    _check(lib().cb_filter_schedule(n_layers, r_first_e4, r_last_e4, n_ctx, n_cand, out), "cb_filter_schedule")
+    return [int(x) for x in out]
+
+
+def workspace_size(cfg: LayerConfig, T: int, m_max: int) -> int:
+    return int(lib().cb_workspace_size(ctypes.byref(cfg), T, m_max))
+
+
+def status_string(s: int) -> str:
+    return lib().cb_status_string(s).decode()
+
+
+def profile_begin():
+    _check(lib().cb_profile_begin(), "cb_profile_begin")
+
+
+def profile_end() -> Dict[str, dict]:
+    out = (KernelStat * 64)()
+    n = lib().cb_profile_end(out, 64)
+    if n < 0:
+        raise CacheBlendError(6, "cb_profile_end", lib().cb_last_hip_error())
+    return {out[i].name.decode(): {"launches": out[i].launches, "total_ms": out[i].total_ms,
+                                   "min_ms": out[i].min_ms, "max_ms": out[i].max_ms} for i in range(min(n, 64))}
+
+
+# ---------------------------------------------------------------------------
+# device objects
+# ---------------------------------------------------------------------------
+
+class DeviceRope:
+    """RoPE table (cb_rope_table) for positions 0 .. n_pos-1, resident on the device."""
+
+    def __init__(self, cfg: LayerConfig, n_pos: int, device="cuda"):
+        torch = _torch()
+        c, s = rope_table(cfg, 0, n_pos)
+        self.cos = torch.from_numpy(c).to(device)
+        self.sin = torch.from_numpy(s).to(device)
+        self.struct = RopeDev(self.cos.data_ptr(), self.sin.data_ptr(), n_pos)
+
+
+class DeviceLayer:
+    """One layer's weights on the device (nn.Linear layout, cfg dtype; gains fp32)."""
+
+    NAMES = ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")
+
+    def __init__(self, cfg: LayerConfig, weights: Dict[str, object], device="cuda"):
+        torch = _torch()
+        dt = torch_dtype(cfg)
+        self.t = {}
+        for k in self.NAMES:
+            v = weights[k]
+            v = v if isinstance(v, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(v))
+            self.t[k] = v.to(device=device, dtype=dt).contiguous()
+        for k in ("attn_norm", "mlp_norm"):
+            v = weights[k]
+            v = v if isinstance(v, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(v))
+            self.t[k] = v.to(device=device, dtype=torch.float32).contiguous()
+        self.struct = LayerWeights(*[self.t[n].data_ptr() for n in
+                                     ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up",
+                                      "w_down")])
+
+
+def workspace(cfg: LayerConfig, T: int, m_max: int, device="cuda"):
+    torch = _torch()
+    n = workspace_size(cfg, T, m_max)
+    if n == 0:
+        raise CacheBlendError(1, "cb_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# device calls
+# ---------------------------------------------------------------------------
+
+def rope_shift(cfg: LayerConfig, rope: DeviceRope, k_cache, layer_stride: int, n_layers: int, T: int,
+               chunk_offsets: Sequence[int], stream=None):
+    offs = np.ascontiguousarray(np.asarray(chunk_offsets, dtype=np.int32))
+    kv = cfg.n_kv_heads * cfg.head_dim
+    need = (n_layers - 1) * layer_stride + T * kv if n_layers > 0 else 0
+    _check(lib().cb_rope_shift(ctypes.byref(cfg), ctypes.byref(rope.struct),
+                               _dptr(k_cache, "k_cache", torch_dtype(cfg), need), layer_stride, n_layers, T,
+                               offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(offs) - 1,
+                               _stream(stream)), "cb_rope_shift")
+
+
+def select_hkvd(cfg: LayerConfig, k_new, k_ref, T: int, cand_rows, n: int, k: int, dev, sel_out, ws, stream=None):
+    torch = _torch()
+    kv = cfg.n_kv_heads * cfg.head_dim
+    _check(lib().cb_select_hkvd(ctypes.byref(cfg), _dptr(k_new, "k_new", torch_dtype(cfg), n * kv),
+                                _dptr(k_ref, "k_ref", torch_dtype(cfg), T * kv if k_new is not None else None),
+                                T, _dptr(cand_rows, "cand_rows", torch.int32, n), n, k,
+                                _dptr(dev, "dev", torch.float32, n), _dptr(sel_out, "sel_out", torch.int32, k),
+                                _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "cb_select_hkvd")
+
+
+def blend_layer(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, k_cache, v_cache, T: int, n_ctx: int,
+                first_chunk_len: int, s_in, m_in: int, hidden_in, in_rows, k_out: int, hidden_out, dev_out, s_out,
+                ws, stream=None) -> int:
+    """One selective-recompute layer; returns m_out (rows of hidden_out / s_out written)."""
+    torch = _torch()
+    dt = torch_dtype(cfg)
+    kv, d = cfg.n_kv_heads * cfg.head_dim, cfg.d_model
+    m_exp = max(expected_m_out(T, n_ctx, m_in, k_out), 0)
+    m_out = ctypes.c_int32(0)
+    _check(lib().cb_blend_layer(ctypes.byref(cfg), ctypes.byref(layer.struct), ctypes.byref(rope.struct),
+                                _dptr(k_cache, "k_cache", dt, T * kv), _dptr(v_cache, "v_cache", dt, T * kv), T,
+                                n_ctx, first_chunk_len, _dptr(s_in, "s_in", torch.int32, m_in), m_in,
+                                _dptr(hidden_in, "hidden_in", dt, (T if in_rows is not None else m_in) * d),
+                                _dptr(in_rows, "in_rows", torch.int32, m_in), k_out,
+                                _dptr(hidden_out, "hidden_out", dt, m_exp * d),
+                                _dptr(dev_out, "dev_out", torch.float32, m_in),
+                                _dptr(s_out, "s_out", torch.int32, m_exp), ctypes.byref(m_out),
+                                _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "cb_blend_layer")
+    return int(m_out.value)
+
+
+def expected_m_out(T: int, n_ctx: int, m_in: int, k_out: int) -> int:
+    """m_out of cb_blend_layer, known on the host before the call."""
+    n_query = T - n_ctx
+    return min(k_out, m_in - n_query) + n_query
+
+
+def full_prefill_layer(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, hidden_in, T: int, pos0: int,
+                       k_out, v_out, hidden_out, ws, stream=None):
+    dt = torch_dtype(cfg)
+    kv, d = cfg.n_kv_heads * cfg.head_dim, cfg.d_model
+    _check(lib().cb_full_prefill_layer(ctypes.byref(cfg), ctypes.byref(layer.struct), ctypes.byref(rope.struct),
+                                       _dptr(hidden_in, "hidden_in", dt, T * d), T, pos0,
+                                       _dptr(k_out, "k_out", dt, T * kv), _dptr(v_out, "v_out", dt, T * kv),
+                                       _dptr(hidden_out, "hidden_out", dt, T * d), _dptr(ws, "ws", _torch().uint8),
+                                       ws.numel(), _stream(stream)), "cb_full_prefill_layer")

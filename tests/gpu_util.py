@@ -1,0 +1,72 @@
+"""Helpers of the GPU parity tests: moving seeded inputs to the device and
+building the oracle side of a case.  Nothing here computes a fusor step."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import blend, layer, prepass, rope
+from oracle.storage import round_store
+from rag_kv_cache_layer_amd import synth
+
+torch = pytest.importorskip("torch")
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def store_of(p):
+    return "bf16" if p.dtype == "bf16" else None
+
+
+def tol_of(p):
+    """max |x - y| / max |y| per tensor: 2e-2 for bf16 storage, 1e-5 for fp32."""
+    return 2e-2 if p.dtype == "bf16" else 1e-5
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dtype)
+
+
+def act_dtype(p):
+    return torch.bfloat16 if p.dtype == "bf16" else torch.float32
+
+
+def host(t):
+    return t.detach().float().cpu().numpy()
+
+
+def rel_err(x, y) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = float(np.max(np.abs(y))) if y.size else 0.0
+    d = float(np.max(np.abs(x - y))) if y.size else 0.0
+    return d / den if den > 0 else d
+
+
+def single_layer_case(p, seed: int, prepass_inputs: bool = True):
+    """Weights, the shifted cache, hidden inputs and geometry of one layer.
+
+    With prepass_inputs the cache holds isolated-prefill K/V and the hidden
+    states are those of a full prefill of the same layer (the tied pre-pass of
+    oracle.prepass); otherwise both are seeded normal draws of the same shape."""
+    st = store_of(p)
+    w = synth.layer_weights(p, seed, 0)
+    order = synth.chunk_order(p, seed)
+    offs = synth.chunk_offsets(p, order)
+    T, kv = p.T, (p.n_kv_heads, p.head_dim)
+    if prepass_inputs:
+        e_chunks = [synth.chunk_embedding(p, seed, c) for c in order]
+        inp = prepass.single_layer_inputs(w, p, e_chunks, synth.query_embedding(p, seed), store=st)
+        k_pre, v_pre, hid = inp["k_pre"], inp["v_pre"], inp["hidden"]
+    else:
+        k_pre = synth.random_normal(p, seed, (T,) + kv, tag_layer=11)
+        v_pre = synth.random_normal(p, seed, (T,) + kv, tag_layer=12)
+        hid = synth.random_normal(p, seed, (T, p.d_model), tag_layer=13)
+        k_pre[p.n_ctx:] = 0
+        v_pre[p.n_ctx:] = 0
+    k_sh = rope.rope_shift(k_pre, offs, p.rope_theta, st)
+    return dict(w=w, offs=offs, k_pre=k_pre, v_pre=v_pre, k=k_sh, v=v_pre.copy(), hidden=hid, T=T,
+                n_ctx=p.n_ctx, L0=int(offs[1]))

@@ -1,0 +1,220 @@
+"""cb_full_prefill_layer and cb_blend_layer against the oracle on seeded
+inputs at sizes the oracle runs in seconds (ragged chunk lengths, several
+GEMM / attention tiles plus tails).
+
+Tolerances (max |x - y| / max |y| per tensor): 2e-2 with bf16 storage, 1e-5
+in fp32.  Index outputs are compared exactly: the kept set must be the
+oracle's top-k of the GPU's own deviation array, and the layer outputs are
+then compared with the oracle run on that same selection."""
+import numpy as np
+import pytest
+
+from oracle import blend, layer
+from rag_kv_cache_layer_amd import fusor as F
+from rag_kv_cache_layer_amd import synth
+from tests.gpu_util import act_dtype, dev, host, need_gpu, rel_err, single_layer_case, store_of, tol_of, torch
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.PRESETS["tiny_f32"]
+# bf16, GQA group 4, head_dim 64, FFN not a multiple of the tile (gate/up and
+# down-projection tails), down projection split in two along K
+MED64 = synth.scaled(synth.PRESETS["llama8b_layer"], 1024, 16, 4, 64, 2776, [100, 77, 150], 13)
+# bf16, GQA group 8, head_dim 128 (the 70B head layout)
+MED128 = synth.scaled(synth.PRESETS["llama70b_stack"], 1024, 8, 1, 128, 2048, [130, 61, 140], 9, n_layers=1)
+# fp32 with GQA and ragged chunks
+F32GQA = synth.scaled(synth.PRESETS["llama8b_layer"], 128, 8, 2, 16, 344, [24, 20, 28], 8).with_(dtype="f32")
+CASES = [TINY, F32GQA, MED64, MED128]
+IDS = ["tiny_f32", "f32_gqa", "bf16_hd64", "bf16_hd128"]
+
+
+class Gpu:
+    """Device copies of one single-layer case."""
+
+    def __init__(self, p, case):
+        self.p, self.c = p, case
+        self.cfg = F.config_of(p)
+        self.ad = act_dtype(p)
+        self.layer = F.DeviceLayer(self.cfg, case["w"])
+        self.rope = F.DeviceRope(self.cfg, p.T)
+        self.ws = F.workspace(self.cfg, p.T, p.T)
+
+    def blend(self, k_cache, v_cache, s_in, hidden, in_rows, k_out):
+        p = self.p
+        kc, vc = dev(k_cache, self.ad), dev(v_cache, self.ad)
+        m_in = len(s_in)
+        m_out = F.expected_m_out(p.T, p.n_ctx, m_in, k_out)
+        hout = torch.zeros((max(m_out, 1), p.d_model), dtype=self.ad, device="cuda")
+        dv = torch.zeros(max(m_in, 1), dtype=torch.float32, device="cuda")
+        so = torch.full((max(m_out, 1),), -1, dtype=torch.int32, device="cuda")
+        m = F.blend_layer(self.cfg, self.layer, self.rope, kc, vc, p.T, p.n_ctx, self.c["L0"],
+                          dev(np.asarray(s_in, np.int32), torch.int32), m_in, dev(hidden, self.ad),
+                          None if in_rows is None else dev(np.asarray(in_rows, np.int32), torch.int32), k_out, hout,
+                          dv, so, self.ws)
+        torch.cuda.synchronize()
+        assert m == m_out
+        return dict(k=host(kc), v=host(vc), y=host(hout)[:m], dev=host(dv)[:m_in], s_out=so.cpu().numpy()[:m])
+
+    def prefill(self, hidden, pos0=0):
+        p = self.p
+        T = hidden.shape[0]
+        kv = (T, p.n_kv_heads, p.head_dim)
+        k = torch.zeros(kv, dtype=self.ad, device="cuda")
+        v = torch.zeros(kv, dtype=self.ad, device="cuda")
+        y = torch.zeros((T, p.d_model), dtype=self.ad, device="cuda")
+        F.full_prefill_layer(self.cfg, self.layer, self.rope, dev(hidden, self.ad), T, pos0, k, v, y, self.ws)
+        torch.cuda.synchronize()
+        return host(k), host(v), host(y)
+
+
+@pytest.mark.parametrize("p", CASES, ids=IDS)
+def test_full_prefill(p):
+    need_gpu()
+    case = single_layer_case(p, 1, prepass_inputs=False)
+    g = Gpu(p, case)
+    x = case["hidden"]
+    k, v, y = g.prefill(x)
+    kw, vw, yw = layer.full_prefill(case["w"], x, p, 0, store=store_of(p))
+    tol = tol_of(p)
+    assert rel_err(k, kw) < tol and rel_err(v, vw) < tol and rel_err(y, yw) < tol
+    # a chunk prefilled alone at a later position (pos0 > 0)
+    k2, v2, y2 = g.prefill(x[:37], pos0=50)
+    kw2, vw2, yw2 = layer.full_prefill(case["w"], x[:37], p, 50, store=store_of(p))
+    assert rel_err(k2, kw2) < tol and rel_err(y2, yw2) < tol
+
+
+@pytest.mark.parametrize("p", [TINY, MED64], ids=["tiny_f32", "bf16_hd64"])
+def test_prefix_invariant_bit_exact(p):
+    """The first chunk's K/V and outputs from a prefill of that chunk alone
+    equal those rows of the full-context prefill bit for bit (prefix caching:
+    the prefix KV does not depend on what follows)."""
+    need_gpu()
+    case = single_layer_case(p, 2, prepass_inputs=False)
+    g = Gpu(p, case)
+    L0 = case["L0"]
+    k, v, y = g.prefill(case["hidden"])
+    k0, v0, y0 = g.prefill(case["hidden"][:L0])
+    assert np.array_equal(k[:L0], k0) and np.array_equal(v[:L0], v0) and np.array_equal(y[:L0], y0)
+
+
+def _check_blend(p, case, got, want, s_in):
+    tol = tol_of(p)
+    T, n_ctx = p.T, p.n_ctx
+    untouched = np.setdiff1d(np.arange(T), s_in)
+    # reused rows are exactly the shifted cache
+    assert np.array_equal(got["k"][untouched], case["k"][untouched])
+    assert np.array_equal(got["v"][untouched], case["v"][untouched])
+    assert rel_err(got["k"], want["k_cache"]) < tol
+    assert rel_err(got["v"], want["v_cache"]) < tol
+    assert rel_err(got["y"], want["y"]) < tol
+    n_cand = int(np.sum(np.asarray(s_in) < n_ctx))
+    assert np.all(np.isnan(got["dev"][n_cand:]))
+    if n_cand:
+        assert rel_err(got["dev"][:n_cand], want["dev"][:n_cand]) < tol
+
+
+@pytest.mark.parametrize("p", CASES, ids=IDS)
+def test_select_then_blend_calls(p):
+    """The two calls of a single-layer workload: the select call recomputes
+    every candidate and keeps the top k (section 4.3), the blend call
+    recomputes only the kept rows (section 4.2)."""
+    need_gpu()
+    case = single_layer_case(p, 0)
+    g = Gpu(p, case)
+    st = store_of(p)
+    T, n_ctx, L0 = p.T, p.n_ctx, case["L0"]
+    k = blend.num_selected(p.r_e4, n_ctx, n_ctx - L0)
+    s_in = np.arange(L0, T)
+    got = g.blend(case["k"], case["v"], s_in, case["hidden"], s_in, k)
+    n_cand = n_ctx - L0
+    keep = blend.topk_hkvd(got["dev"][:n_cand], k)          # oracle ranking of the GPU's deviations
+    assert np.array_equal(got["s_out"], np.concatenate([s_in[keep], np.arange(n_ctx, T)]))
+    want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_in, case["hidden"][s_in], k, store=st,
+                             keep=keep)
+    _check_blend(p, case, got, want, s_in)
+    # free-running agreement of the two selections (reported, not gated)
+    own = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_in, case["hidden"][s_in], k, store=st)
+    a, b = set(own["s_out"][:k].tolist()), set(got["s_out"][:k].tolist())
+    print(f"\n{p.name}: jaccard(GPU, oracle selection) = {len(a & b) / max(len(a | b), 1):.4f}")
+    # blend call: recompute the kept rows on the cache the select call produced
+    s2 = want["s_out"]
+    got2 = g.blend(want["k_cache"], want["v_cache"], s2, case["hidden"], s2, k)
+    want2 = blend.blend_layer(case["w"], p, want["k_cache"], want["v_cache"], n_ctx, s2, case["hidden"][s2], k,
+                              store=st)
+    assert np.array_equal(got2["s_out"], s2)
+    case2 = dict(case, k=want["k_cache"], v=want["v_cache"])
+    _check_blend(p, case2, got2, want2, s2)
+
+
+@pytest.mark.parametrize("p", [TINY, MED64], ids=["tiny_f32", "bf16_hd64"])
+def test_blend_degenerate_cases(p):
+    """k = 0 (full KV reuse: only the query is recomputed), k >= candidates
+    (r = 1: every row), a query-only input, and a single cached chunk
+    (prefix caching)."""
+    need_gpu()
+    case = single_layer_case(p, 3, prepass_inputs=False)
+    g = Gpu(p, case)
+    st = store_of(p)
+    T, n_ctx, L0 = p.T, p.n_ctx, case["L0"]
+    s_all = np.arange(L0, T)
+    for k in (0, n_ctx - L0, n_ctx):
+        got = g.blend(case["k"], case["v"], s_all, case["hidden"], s_all, k)
+        want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_all, case["hidden"][s_all], k,
+                                 store=st, keep=None if k else np.zeros(0, np.int64))
+        if k:
+            assert np.array_equal(got["s_out"], s_all)
+        else:
+            assert np.array_equal(got["s_out"], np.arange(n_ctx, T))
+        _check_blend(p, case, got, want, s_all)
+    q_only = np.arange(n_ctx, T)
+    got = g.blend(case["k"], case["v"], q_only, case["hidden"][n_ctx:], None, 5)
+    want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, q_only, case["hidden"][n_ctx:], 5, store=st)
+    assert np.array_equal(got["s_out"], q_only)
+    _check_blend(p, case, got, want, q_only)
+
+
+def test_r1_blend_equals_full_prefill_gpu():
+    """r = 1 on a layer whose cache and inputs come from full prefill gives
+    full prefill back (section 4.2: r% of the tokens -> 100% is full prefill)."""
+    need_gpu()
+    p = TINY
+    case = single_layer_case(p, 4, prepass_inputs=False)
+    g = Gpu(p, case)
+    x = case["hidden"]
+    k, v, y = g.prefill(x)
+    L0 = case["L0"]
+    s_all = np.arange(L0, p.T)
+    got = g.blend(k, v, s_all, x, s_all, p.T)
+    assert rel_err(got["k"], k) < 1e-5 and rel_err(got["v"], v) < 1e-5 and rel_err(got["y"], y[L0:]) < 1e-5
+    assert np.max(got["dev"][:p.n_ctx - L0]) < 1e-8
+
+
+def test_stack_teacher_forced_gradual_filtering():
+    """Three layers with gradual filtering (section 4.3, Figure 9): layer 0
+    recomputes every candidate, layer 1 selects, layer 2 filters within that
+    set.  Each GPU layer is given the oracle's input of that layer."""
+    need_gpu()
+    p = synth.scaled(synth.PRESETS["llama8b_stack"], 512, 8, 2, 64, 1024, [60, 45, 70, 33], 7, n_layers=3)
+    st = "bf16"
+    ws_ = [synth.layer_weights(p, 9, l) for l in range(3)]
+    order = synth.chunk_order(p, 9)
+    offs = synth.chunk_offsets(p, order)
+    kv = {c: blend.precompute_chunk(ws_, p, synth.chunk_embedding(p, 9, c), store=st) for c in order}
+    K, V = blend.assemble_caches(p, kv, order, p.T, 3)
+    K = blend.shift_caches(p, K, offs, st)
+    x_all = synth.context_embeddings(p, 9, order)
+    n_ctx, L0 = p.n_ctx, int(offs[1])
+    ks = blend.filter_schedule(3, 3000, 1500, n_ctx, n_ctx - L0)
+    assert ks == F.filter_schedule(3, 3000, 1500, n_ctx, n_ctx - L0)
+    s = np.arange(L0, p.T)
+    x = x_all[s]
+    for l in range(3):
+        g = Gpu(p, dict(w=ws_[l], L0=L0, k=K[l], v=V[l]))
+        got = g.blend(K[l], V[l], s, x, None, ks[l])
+        n_cand = int(np.sum(s < n_ctx))
+        keep = blend.topk_hkvd(got["dev"][:n_cand], min(ks[l], n_cand))
+        want = blend.blend_layer(ws_[l], p, K[l], V[l], n_ctx, s, x, ks[l], store=st, keep=keep)
+        assert np.array_equal(got["s_out"], want["s_out"])
+        _check_blend(p, dict(k=K[l], v=V[l]), got, want, s)
+        s, x = want["s_out"], want["y"]
+        assert len(s) == min(ks[l], n_cand) + p.query_len
