@@ -122,10 +122,11 @@ def main():
     hout = torch.empty((m, d), dtype=bf, device=dev)
     s_out = torch.empty(m, dtype=torch.int32, device=dev)
     dv = torch.empty(m, dtype=torch.float32, device=dev)
-    # the step works on its own copies of the cache; repeated steps rotate the
-    # same rows again and rewrite the same recomputed rows, at identical cost
+    # the step works on its own copy of the precomputed cache; repeated steps
+    # rotate the same rows again and rewrite the same recomputed rows, at
+    # identical cost
     kb = k_pre.clone()
-    vb = v_cache.clone()
+    vb = v_pre.clone()
 
     def step():
         F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)

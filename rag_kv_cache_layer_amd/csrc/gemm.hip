@@ -202,35 +202,29 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
   const int ke = min(K, kb + kchunk);
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
-  const bf16_t* aptr[4];
-  const bf16_t* bptr[4];
+  // Loader: each thread moves 4 A and 4 B chunks of 16 B per K step.  The
+  // addresses are always in bounds (invalid rows fall back to row 0 / the
+  // weight's first row, the K tail to the first chunk of this split) and the
+  // zero fill is applied when the chunk is written to LDS, so no loaded value
+  // is consumed before the MFMAs of the current step have been issued.
+  typedef __attribute__((address_space(1))) const u32x4_t guint4;
+  const guint4* ag[4];
+  const guint4* bg[4];
+  bool aok[4], bok[4];
   int lrow[4], lcol[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + 256 * i;
     lrow[i] = c >> 3;
     lcol[i] = (c & 7) * 8;
-    aptr[i] = (m0 + lrow[i] < M) ? (const bf16_t*)g.A + (int64_t)(m0 + lrow[i]) * K + lcol[i] : nullptr;
+    aok[i] = m0 + lrow[i] < M;
+    ag[i] = (const guint4*)((const bf16_t*)g.A + (int64_t)(aok[i] ? m0 + lrow[i] : 0) * K);
     const bf16_t* br = b_row<bf16_t>(g.B, K, g.N, tn, BN, lrow[i]);
-    bptr[i] = br ? br + lcol[i] : nullptr;
+    bok[i] = br != nullptr;
+    bg[i] = (const guint4*)(bok[i] ? br : (const bf16_t*)g.B.p0);
   }
-  uint4 ra[4], rb[4];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool kin = k0 + lcol[i] < ke;
-      ra[i] = (aptr[i] && kin) ? *reinterpret_cast<const uint4*>(aptr[i] + k0) : z4;
-      rb[i] = (bptr[i] && kin) ? *reinterpret_cast<const uint4*>(bptr[i] + k0) : z4;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(As + (buf * BM + lrow[i]) * LDK + lcol[i]) = ra[i];
-      *reinterpret_cast<uint4*>(Bs + (buf * BN + lrow[i]) * LDK + lcol[i]) = rb[i];
-    }
-  };
+  u32x4_t ra[4], rb[4];
+  const u32x4_t z4 = {0u, 0u, 0u, 0u};
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -241,13 +235,34 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   if (nk > 0) {
-    gload(kb);
-    lstore(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kk = kb + lcol[i];
+      const int kc = (kk < ke ? kk : kb) >> 3;
+      ra[i] = ag[i][kc];
+      rb[i] = bg[i][kc];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool kin = kb + lcol[i] < ke;
+      *reinterpret_cast<u32x4_t*>(As + lrow[i] * LDK + lcol[i]) = (aok[i] && kin) ? ra[i] : z4;
+      *reinterpret_cast<u32x4_t*>(Bs + lrow[i] * LDK + lcol[i]) = (bok[i] && kin) ? rb[i] : z4;
+    }
   }
   __syncthreads();
   for (int it = 0; it < nk; ++it) {
     const int cur = it & 1;
-    if (it + 1 < nk) gload(kb + (it + 1) * BK);
+    const int kn = kb + (it + 1) * BK;  // next K step
+    const bool more = it + 1 < nk;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kn + lcol[i];
+        const int kc = (kk < ke ? kk : kb) >> 3;
+        ra[i] = ag[i][kc];
+        rb[i] = bg[i][kc];
+      }
+    }
     const bf16_t* Ac = As + cur * BM * LDK;
     const bf16_t* Bc = Bs + cur * BN * LDK;
 #pragma unroll
@@ -264,7 +279,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (it + 1 < nk) lstore(cur ^ 1);
+    if (more) {
+      bf16_t* An = As + (cur ^ 1) * BM * LDK;
+      bf16_t* Bn = Bs + (cur ^ 1) * BN * LDK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool kin = kn + lcol[i] < ke;
+        *reinterpret_cast<u32x4_t*>(An + lrow[i] * LDK + lcol[i]) = (aok[i] && kin) ? ra[i] : z4;
+        *reinterpret_cast<u32x4_t*>(Bn + lrow[i] * LDK + lcol[i]) = (bok[i] && kin) ? rb[i] : z4;
+      }
+    }
     __syncthreads();
   }
 

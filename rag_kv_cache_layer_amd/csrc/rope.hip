@@ -48,12 +48,16 @@ __global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int6
   const float* sn = sinp + (int64_t)delta * (hd / 2) + e / 2;
   float v[8], o[8];
   load8(p, v);
+  {
+    // two rounded products and one rounded sum per output: no contraction
+    // into fused multiply-adds in this block
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float a = v[2 * j], b = v[2 * j + 1], c = cs[j], s = sn[j];
-    // two rounded products and one rounded sum per output, no fused multiply-add
-    o[2 * j] = __fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s));
-    o[2 * j + 1] = __fadd_rn(__fmul_rn(a, s), __fmul_rn(b, c));
+    for (int j = 0; j < 4; ++j) {
+      const float a = v[2 * j], b = v[2 * j + 1], c = cs[j], s = sn[j];
+      o[2 * j] = a * c - b * s;
+      o[2 * j + 1] = a * s + b * c;
+    }
   }
   store8(p, o);
 }
