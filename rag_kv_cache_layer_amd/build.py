@@ -32,24 +32,27 @@ def _run(cmd):
     return r.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
+    """Compile every source and link the shared library; returns its path.
+    defines: extra -D macros (kernel tuning knobs); out / build_dir: where the
+    objects and the library go."""
+    os.makedirs(build_dir, exist_ok=True)
+    objs = [os.path.join(build_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[HIPCC, *FLAGS, *["-D" + d for d in defines], "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(cmds))) as ex:
         results = list(ex.map(_run, cmds))
-    for cmd, (rc, out) in zip(cmds, results):
-        if verbose and out.strip():
-            print(out, file=sys.stderr)
+    for cmd, (rc, log) in zip(cmds, results):
+        if verbose and log.strip():
+            print(log, file=sys.stderr)
         if rc != 0:
-            raise RuntimeError("hipcc failed: " + " ".join(cmd) + "\n" + out)
-    tmp = LIB + ".tmp"
-    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+            raise RuntimeError("hipcc failed: " + " ".join(cmd) + "\n" + log)
+    tmp = out + ".tmp"
+    rc, log = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     if rc != 0:
-        raise RuntimeError("link failed\n" + out)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("link failed\n" + log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -111,7 +111,7 @@ struct Dims {
 };
 
 struct Ws {
-  size_t xn, q, devp, dev, sel, o, h, hn, u, part, scratch, total;
+  size_t xn, q, devp, dev, sel, o, h, hn, u, part, o_part, ml_part, scratch, total;
 };
 
 BOperand b_single(const void* p, int n) {
@@ -142,7 +142,8 @@ size_t part_floats(int dtype, const Dims& D, int m) {
   return best;
 }
 
-Ws layout(const cb_layer_config& c, int m) {
+// Workspace for up to m rows over a cache of T rows.
+Ws layout(const cb_layer_config& c, int m, int T) {
   const Dims D(c);
   Ws w{};
   size_t off = 0;
@@ -162,6 +163,11 @@ Ws layout(const cb_layer_config& c, int m) {
   w.hn = take(M * D.d * D.b);
   w.u = take(M * D.F * D.b);
   w.part = take(part_floats(c.dtype, D, (int)M) * 4);
+  // attention key-split partials: only for row counts that use the split
+  const size_t arows = std::min(M, attn_part_rows(c.n_kv_heads));
+  const size_t nsplit = c.dtype == CB_BF16 ? (size_t)(std::max(T, 1) + 511) / 512 : 0;
+  w.o_part = take(nsplit * arows * D.q_dim * 4);
+  w.ml_part = take(nsplit * arows * c.n_q_heads * 8);
   w.scratch = take(256);
   w.total = off;
   return w;
@@ -341,7 +347,7 @@ extern "C" cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, in
 
 extern "C" size_t cb_workspace_size(const cb_layer_config* cfg, int32_t T, int32_t m_max) {
   if (check_cfg(cfg) != CB_OK || T < 0 || m_max < 0) return 0;
-  return layout(*cfg, std::max(T, m_max)).total;
+  return layout(*cfg, std::max(T, m_max), T).total;
 }
 
 extern "C" const char* cb_status_string(cb_status s) {
@@ -496,7 +502,7 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   if (m_in == 0) return CB_OK;
 
   const Dims D(*cfg);
-  const Ws L = layout(*cfg, m_in);
+  const Ws L = layout(*cfg, std::max(T, m_in), T);
   hipStream_t s = (hipStream_t)stream;
   const int dt = cfg->dtype;
   const int n_src = in_rows ? T : m_in;
@@ -544,6 +550,9 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   aa.n_q = cfg->n_q_heads;
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
+  aa.key_split = attn_key_split(dt, m_out, cfg->n_kv_heads);
+  aa.o_part = at<float>(ws, L.o_part);
+  aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
   // 5. O projection, MLP
@@ -568,7 +577,7 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   if (ws_bytes < cb_workspace_size(cfg, T, T)) return CB_ERR_WORKSPACE;
   if (T == 0) return CB_OK;
   const Dims D(*cfg);
-  const Ws L = layout(*cfg, T);
+  const Ws L = layout(*cfg, T, T);
   hipStream_t s = (hipStream_t)stream;
   const int dt = cfg->dtype;
   st = hip_status(launch_rmsnorm(dt, false, hidden_in, T, nullptr, nullptr, (const float*)w->attn_norm,
@@ -593,6 +602,9 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   aa.n_q = cfg->n_q_heads;
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
+  aa.key_split = attn_key_split(dt, T, cfg->n_kv_heads);
+  aa.o_part = at<float>(ws, L.o_part);
+  aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
   return layer_tail(*cfg, *w, L, ws, T, hidden_in, T, nullptr, nullptr, hidden_out, s);

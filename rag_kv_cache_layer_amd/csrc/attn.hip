@@ -7,19 +7,27 @@
 // cache row / position p_i) attends causally to cache rows 0 .. p_i; query
 // head h reads KV head h / (n_q / n_kv).
 //
-// bf16 path (gfx950 matrix cores): one workgroup per (16 query rows, KV head)
-// with one wave per query head of the group, so the K/V tiles staged in LDS
-// are shared by all heads that read them.  Each wave keeps its 16 queries'
-// Q fragments in registers and walks 64-key tiles with an online softmax in
-// fp32 (base-2 exponent).  Scores are formed transposed, S^T = K Q^T
-// (v_mfma_f32_16x16x32_bf16), so every lane owns one query column: the
-// row statistics need only two cross-lane steps and the probabilities feed
-// the P V product (O^T += V^T P^T) straight from registers -- the K index of
-// an MFMA is a sum, so the same key permutation on both operands is exact.
-// V is stored transposed in LDS for that product.  A key tile past a query's
-// position is an exact no-op for it (alpha = 1, p = 0), so a row's result
-// does not depend on the other rows of its tile.  Tiles holding the latest
-// positions (the longest key ranges) are launched first.
+// bf16 path (gfx950 matrix cores): one workgroup per (32 query rows, KV head,
+// key split) with one wave per query head of the group, so the K/V tiles
+// staged in LDS are shared by all heads that read them.  Each wave keeps its
+// 32 queries' Q fragments in registers (two 16-column MFMA blocks, so every
+// K or V fragment read from LDS feeds two MFMAs) and walks 64-key tiles with
+// an online softmax in fp32 (base-2 exponent); the next tile's loads are in
+// flight while the current one is computed.  Scores are formed transposed,
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so every lane owns one query column:
+// the row statistics need only two cross-lane steps and the probabilities
+// feed the P V product (O^T += V^T P^T) straight from registers -- the K index
+// of an MFMA is a sum, so the same key permutation on both operands is exact.
+// V is stored transposed in LDS (8-byte stores of 4 keys) for that product.
+// A key tile past a query's position is an exact no-op for it (alpha = 1,
+// p = 0), so a row's result does not depend on the other rows of its tile.
+// Tiles holding the latest positions (the longest key ranges) go first.
+//
+// When there are too few (row tile, KV head) workgroups to fill the chip, the
+// keys are split at fixed multiples of 512: each split writes an unnormalised
+// partial (O, running max, sum) and a merge kernel combines a row's splits in
+// split order.  The split boundaries never depend on the other rows, so a row's
+// result still does not either.
 //
 // fp32 path: one wave per (row, head); scores in LDS, two-pass softmax.
 #include "cb_internal.h"
@@ -28,116 +36,166 @@ namespace cb {
 
 namespace {
 
+constexpr int kRowTile = 32;     // query rows per workgroup (two 16-column MFMA blocks per wave)
+constexpr int kKeyTile = 64;     // keys per LDS stage
+constexpr int kKeySplit = 512;   // key-split boundary (multiple of kKeyTile)
+
 template <int HD, int G>
-__global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
   constexpr int NT = 64 * G;
-  constexpr int KT = 64;
-  constexpr int KLD = HD + 8;
-  constexpr int VLD = KT + 8;
+  constexpr int KT = kKeyTile;
+  constexpr int KLD = HD + 8;                 // K tile row stride (bf16)
+  constexpr int VLD = KT + 8;                 // V^T tile row stride (bf16)
+  constexpr int UNITS = (KT / 4) * (HD / 8);  // 4 keys x 8 dims per unit
+  constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
+  constexpr bool PREFETCH = UPT <= 2;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[KT * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VLD];
-  const int n_tiles = (a.m + 15) / 16;
-  const int tile = n_tiles - 1 - (int)blockIdx.x;
+  typedef __attribute__((address_space(1))) const u32x4_t gvec;
+
+  const int n_tiles = (a.m + kRowTile - 1) / kRowTile;
+  const int tile = n_tiles - 1 - (int)blockIdx.x;   // latest positions (longest key ranges) first
   const int kvh = blockIdx.y;
+  const int split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = kvh * G + w;
   const int q = lane & 15, gp = lane >> 4;
-  const int i = tile * 16 + q;
-  const bool valid = i < a.m;
-  int p = valid ? (a.qpos ? a.qpos[i] : i) : 0;
-  p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
-  int pm = p;
+
+  int pos[2];
+  bool valid[2];
+  int pm = 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int i = tile * kRowTile + b * 16 + q;
+    valid[b] = i < a.m;
+    int p = valid[b] ? (a.qpos ? a.qpos[i] : i) : 0;
+    pos[b] = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+    pm = max(pm, pos[b]);
+  }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) pm = max(pm, __shfl_xor(pm, o));
+  // key range of this workgroup
+  const bool splitting = a.key_split > 0 && pm >= a.key_split;
+  const int k_lo = a.key_split > 0 ? split * a.key_split : 0;
+  const int k_hi = splitting ? min(pm + 1, k_lo + a.key_split) : pm + 1;
+  if (k_lo >= k_hi) return;   // uniform over the workgroup
 
   const int ldq = a.n_q * HD, ldkv = a.n_kv * HD;
-  bf16x8_t qf[HD / 32];
-  {
-    const int qr = valid ? (a.qmap ? a.qmap[i] : i) : 0;
-    const bf16_t* Qp = (const bf16_t*)a.Q + (int64_t)qr * ldq + head * HD + gp * 8;
+  bf16x8_t qf[2][HD / 32];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int i = tile * kRowTile + b * 16 + q;
+    const int qr = valid[b] ? (a.qmap ? a.qmap[i] : i) : 0;
+    const gvec* Qp = (const gvec*)((const bf16_t*)a.Q + (int64_t)qr * ldq + head * HD + gp * 8);
 #pragma unroll
     for (int ks = 0; ks < HD / 32; ++ks) {
-      uint4 u = valid ? *reinterpret_cast<const uint4*>(Qp + ks * 32) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, u);
+      u32x4_t u = valid[b] ? Qp[ks * 4] : u32x4_t{0u, 0u, 0u, 0u};
+      qf[b][ks] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
-  f32x4_t oacc[HD / 16];
+  f32x4_t oacc[2][HD / 16];
 #pragma unroll
-  for (int mb = 0; mb < HD / 16; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const bf16_t* Kg = (const bf16_t*)a.K + kvh * HD;
   const bf16_t* Vg = (const bf16_t*)a.V + kvh * HD;
 
-  for (int t0 = 0; t0 <= pm; t0 += KT) {
-    for (int c = tid; c < KT * HD / 8; c += NT) {
-      const int r = c / (HD / 8), cc = (c % (HD / 8)) * 8;
-      const int t = t0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (t < a.T) {
-        kv = *reinterpret_cast<const uint4*>(Kg + (int64_t)t * ldkv + cc);
-        vv = *reinterpret_cast<const uint4*>(Vg + (int64_t)t * ldkv + cc);
-      }
-      *reinterpret_cast<uint4*>(Ks + r * KLD + cc) = kv;
-      const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+  // staging: unit u = (key group kg of 4 keys, dim chunk dc of 8 dims)
+  u32x4_t rk[UPT][4], rv[UPT][4];
+  // threads past the last unit load a valid duplicate and never store it,
+  // so the loads carry no branch
+#define CB_ATTN_FETCH(T0)                                                  \
+  _Pragma("unroll") for (int j = 0; j < UPT; ++j) {                        \
+    const int u = min(tid + j * NT, UNITS - 1);                            \
+    const int kg = u % (KT / 4), dc = u / (KT / 4);                        \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                        \
+      int t = (T0) + kg * 4 + r;                                           \
+      t = t < a.T ? t : a.T - 1; /* keys past T are masked below */       \
+      rk[j][r] = *(const gvec*)(Kg + (int64_t)t * ldkv + dc * 8);          \
+      rv[j][r] = *(const gvec*)(Vg + (int64_t)t * ldkv + dc * 8);          \
+    }                                                                      \
+  }
+
+  if (PREFETCH) { CB_ATTN_FETCH(k_lo) }
+  for (int t0 = k_lo; t0 < k_hi; t0 += KT) {
+    if (!PREFETCH) { CB_ATTN_FETCH(t0) }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Vt[(cc + 2 * j) * VLD + r] = (bf16_t)(wv[j] & 0xffffu);
-        Vt[(cc + 2 * j + 1) * VLD + r] = (bf16_t)(wv[j] >> 16);
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + j * NT;
+      if (UNITS % NT != 0 && u >= UNITS) continue;
+      const int kg = u % (KT / 4), dc = u / (KT / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *(u32x4_t*)(Ks + (kg * 4 + r) * KLD + dc * 8) = rk[j][r];
+      // V^T: dims dc*8 .. +7, keys kg*4 .. +3 as one 8-byte store per dim
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wsel = e >> 1, sh = (e & 1) * 16;
+        const uint32_t v0 = (rv[j][0][wsel] >> sh) & 0xffffu, v1 = (rv[j][1][wsel] >> sh) & 0xffffu;
+        const uint32_t v2 = (rv[j][2][wsel] >> sh) & 0xffffu, v3 = (rv[j][3][wsel] >> sh) & 0xffffu;
+        *(uint2*)(Vt + (dc * 8 + e) * VLD + kg * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
       }
     }
     __syncthreads();
+    if (PREFETCH && t0 + KT < k_hi) { CB_ATTN_FETCH(t0 + KT) }   // next tile's loads overlap this tile's math
 
-    // S^T[key][query] for 4 blocks of 16 keys; lane holds keys 16kb+4gp+v of query q
-    f32x4_t s[4];
+    // S^T[key][query]: lane holds keys t0+16kb+4gp+v of queries q (b=0) and 16+q (b=1)
+    f32x4_t s[2][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < HD / 32; ++ks) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 16 + q) * KLD + ks * 32 + gp * 8);
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
+        s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
       }
     }
-    float mx = -INFINITY;
+    bf16x8_t pb[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int b = 0; b < 2; ++b) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int key = t0 + kb * 16 + 4 * gp + v;
-        const float x = key <= p ? s[kb][v] * scale_log2 : -INFINITY;
-        s[kb][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float sum = 0.f;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int v = 0; v < 4; ++v) {
+          const int key = t0 + kb * 16 + 4 * gp + v;
+          const float x = key <= pos[b] ? s[b][kb][v] * scale_log2 : -INFINITY;
+          s[b][kb][v] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[b], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
+      const float alpha = exp2f(m_run[b] - m_use);
+      float sum = 0.f;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float e = exp2f(s[kb][v] - m_new);
-        s[kb][v] = e;
-        sum += e;
-      }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    l_run = l_run * alpha + sum;
-    m_run = m_new;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int mb = 0; mb < HD / 16; ++mb) oacc[mb] *= alpha;
-
-    // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j (j<4)
-    // or 32st+16+4gp+(j-4) (j>=4), matching the A operand read from V^T below.
-    bf16x8_t pb[2];
+        for (int v = 0; v < 4; ++v) {
+          const float e = exp2f(s[b][kb][v] - m_use);
+          s[b][kb][v] = e;
+          sum += e;
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l_run[b] = l_run[b] * alpha + sum;
+      m_run[b] = m_new;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha;
+      // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j
+      // (j<4) or 32st+16+4gp+(j-4), matching the V^T reads below
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        pb[st][v] = (__bf16)s[2 * st][v];
-        pb[st][4 + v] = (__bf16)s[2 * st + 1][v];
-      }
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          pb[b][st][v] = (__bf16)s[b][2 * st][v];
+          pb[b][st][4 + v] = (__bf16)s[b][2 * st + 1][v];
+        }
+    }
 #pragma unroll
     for (int mb = 0; mb < HD / 16; ++mb)
 #pragma unroll
@@ -146,20 +204,86 @@ __global__ __launch_bounds__(64 * G) void attn_bf16_kernel(AttnArgs a, float sca
         const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vr);
         const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vr + 16);
         const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[st], oacc[mb], 0, 0, 0);
+        oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
+        oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
       }
     __syncthreads();
   }
+#undef CB_ATTN_FETCH
 
-  if (valid) {
-    const float inv = 1.0f / l_run;
-    bf16_t* Op = (bf16_t*)a.O + (int64_t)i * ldq + head * HD + 4 * gp;
 #pragma unroll
-    for (int mb = 0; mb < HD / 16; ++mb) {
-      const uint32_t w0 = (uint32_t)f2bf(oacc[mb][0] * inv) | ((uint32_t)f2bf(oacc[mb][1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)f2bf(oacc[mb][2] * inv) | ((uint32_t)f2bf(oacc[mb][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(Op + mb * 16) = make_uint2(w0, w1);
+  for (int b = 0; b < 2; ++b) {
+    if (!valid[b]) continue;
+    const int i = tile * kRowTile + b * 16 + q;
+    if (!splitting) {
+      bf16_t* Op = (bf16_t*)a.O + (int64_t)i * ldq + head * HD + 4 * gp;
+#pragma unroll
+      for (int mb = 0; mb < HD / 16; ++mb) {
+        float o[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = oacc[b][mb][v] / l_run[b];
+        const uint32_t w0 = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+        const uint32_t w1 = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+        *reinterpret_cast<uint2*>(Op + mb * 16) = make_uint2(w0, w1);
+      }
+    } else {
+      // unnormalised partial of this key split, merged by attn_merge_kernel
+      const int64_t slot = ((int64_t)split * a.m + i) * a.n_q + head;
+      float* Op = a.o_part + slot * HD + 4 * gp;
+#pragma unroll
+      for (int mb = 0; mb < HD / 16; ++mb)
+        *reinterpret_cast<float4*>(Op + mb * 16) =
+            make_float4(oacc[b][mb][0], oacc[b][mb][1], oacc[b][mb][2], oacc[b][mb][3]);
+      if (gp == 0) *reinterpret_cast<float2*>(a.ml_part + slot * 2) = make_float2(m_run[b], l_run[b]);
     }
+  }
+}
+
+// Merge the key-split partials of one row in split order, for every head:
+// out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s over the splits that
+// hold keys of the row.  Rows of tiles that were not split are skipped.  One
+// workgroup per row; each thread owns 4 consecutive dims of one head.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  __shared__ int s_pm;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int tile = i / kRowTile;
+  if (tid < 64) {
+    const int r = tile * kRowTile + tid;
+    int p = 0;
+    if (tid < kRowTile && r < a.m) {
+      p = a.qpos ? a.qpos[r] : r;
+      p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o));
+    if (tid == 0) s_pm = p;
+  }
+  __syncthreads();
+  if (s_pm < a.key_split) return;   // this tile was written directly
+  int p = a.qpos ? a.qpos[i] : i;
+  p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+  const int ns = p / a.key_split + 1;
+  const int per_row = a.n_q * HD;
+  for (int c = tid * 4; c < per_row; c += 256 * 4) {
+    const int head = c / HD;
+    float m = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, a.ml_part[(((int64_t)sp * a.m + i) * a.n_q + head) * 2]);
+    float den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < ns; ++sp) {
+      const int64_t slot = ((int64_t)sp * a.m + i) * a.n_q + head;
+      const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
+      const float wgt = exp2f(ml.x - m);
+      den += wgt * ml.y;
+      const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + (c % HD));
+      num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;
+    }
+    bf16_t* Op = (bf16_t*)a.O + (int64_t)i * per_row + c;
+    const uint32_t w0 = (uint32_t)f2bf(num.x / den) | ((uint32_t)f2bf(num.y / den) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(num.z / den) | ((uint32_t)f2bf(num.w / den) << 16);
+    *reinterpret_cast<uint2*>(Op) = make_uint2(w0, w1);
   }
 }
 
@@ -209,22 +333,37 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, float scale) {
 template <int HD>
 hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
   const int g = a.n_q / a.n_kv;
-  const dim3 grid((a.m + 15) / 16, a.n_kv);
-  switch (g) {
-    case 1: attn_bf16_kernel<HD, 1><<<grid, 64, 0, s>>>(a, scale_log2); break;
-    case 2: attn_bf16_kernel<HD, 2><<<grid, 128, 0, s>>>(a, scale_log2); break;
-    case 4: attn_bf16_kernel<HD, 4><<<grid, 256, 0, s>>>(a, scale_log2); break;
-    case 8: attn_bf16_kernel<HD, 8><<<grid, 512, 0, s>>>(a, scale_log2); break;
-    default: return hipErrorInvalidValue;
+  const int n_split = a.key_split > 0 ? (a.T + a.key_split - 1) / a.key_split : 1;
+  const dim3 grid((a.m + kRowTile - 1) / kRowTile, a.n_kv, n_split);
+  {
+    LaunchScope ls("attention", s);
+    switch (g) {
+      case 1: attn_bf16_kernel<HD, 1><<<grid, 64, 0, s>>>(a, scale_log2); break;
+      case 2: attn_bf16_kernel<HD, 2><<<grid, 128, 0, s>>>(a, scale_log2); break;
+      case 4: attn_bf16_kernel<HD, 4><<<grid, 256, 0, s>>>(a, scale_log2); break;
+      case 8: attn_bf16_kernel<HD, 8><<<grid, 512, 0, s>>>(a, scale_log2); break;
+      default: return hipErrorInvalidValue;
+    }
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.key_split <= 0) return e;
+  LaunchScope ls("attn_merge", s);
+  attn_merge_kernel<HD><<<a.m, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int attn_key_split(int dtype, int m, int n_kv) {
+  if (dtype != CB_BF16) return 0;
+  const int blocks = (m + kRowTile - 1) / kRowTile * n_kv;
+  return blocks < 512 ? kKeySplit : 0;
+}
+
+size_t attn_part_rows(int n_kv) { return (size_t)kRowTile * ((512 + n_kv - 1) / n_kv); }
+
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
   if (a.m <= 0) return hipSuccess;
-  LaunchScope ls("attention", s);
   if (dtype == CB_BF16) {
     const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)a.hd));
     if (a.hd == 128) return launch_bf16_hd<128>(a, s, scale_log2);
@@ -232,6 +371,7 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   const float scale = (float)(1.0 / __builtin_sqrt((double)a.hd));
+  LaunchScope ls("attention", s);
   attn_f32_kernel<<<dim3(a.m, a.n_q), 64, (size_t)a.T * sizeof(float), s>>>(a, scale);
   return hipGetLastError();
 }

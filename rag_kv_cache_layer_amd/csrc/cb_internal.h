@@ -190,7 +190,14 @@ struct AttnArgs {
   const void* V;
   void* O;                // [m][n_q*hd]
   int m, T, n_q, n_kv, hd;
+  int key_split;          // 0: one pass over all keys; else keys split at multiples of this
+  float* o_part;          // [T / key_split][m][n_q][hd] unnormalised partials (key_split > 0)
+  float* ml_part;         // [T / key_split][m][n_q][2] running max (log2 units) and sum
 };
+// Key-split length used for m query rows (0 = none); chosen from the row and
+// head counts only.  attn_part_rows bounds the m for which it is non-zero.
+int attn_key_split(int dtype, int m, int n_kv);
+size_t attn_part_rows(int n_kv);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 }  // namespace cb

@@ -6,15 +6,25 @@
 // matrices -- the part of the fusor that really is GEMM-shaped.  B is the
 // nn.Linear weight [out][in], so both operands are contiguous along K.
 //
-// bf16 path (gfx950 matrix cores): 256 threads, 128x128 output tile, K step
-// 64, four waves of 64x64, each a 4x4 grid of v_mfma_f32_16x16x32_bf16.
-// Operands are staged through double-buffered LDS (rows padded by 16 B so the
-// 16-byte fragment reads of 16 rows hit distinct banks).  Tiles are numbered
-// so that the M tiles sharing one weight tile run back to back on the same
-// XCD (workgroups are dealt round-robin to the 8 XCDs), which keeps each
-// weight tile in that XCD's L2 while it is reused.  Split-K (chosen from N
-// and K only, never from M) writes fp32 partials that a second kernel sums in
-// a fixed order, so a row's result never depends on how many rows there are.
+// bf16 path (gfx950 matrix cores).  Operand tiles go from HBM/L2 straight to
+// LDS with buffer loads that write LDS (no VGPR staging); a buffer resource
+// per operand turns rows past the matrix and K past the split into zero
+// fills.  Rows of the LDS tiles are XOR-swizzled by 16-byte chunk so the
+// 16-row fragment reads hit every bank once.  A ring of LDS stages keeps
+// several K steps in flight; each wave waits only for its own loads of the
+// step it needs (vmcnt) and then meets the others at a plain barrier (a fenced
+// barrier would drain the ring).  Two tile shapes:
+//  * 128x128, K step 64, 3-stage ring, four waves of 64x64 (4x4 blocks of
+//    v_mfma_f32_16x16x32_bf16): QKV, O and down projections;
+//  * 256x256, K step 32, 4-stage ring, four waves of 128x128 (accumulators
+//    in AGPRs): the gate/up projection, where N is large -- four times the
+//    matrix work per barrier.
+// Tiles are numbered so that the M tiles sharing one weight tile run back to
+// back on the same XCD (workgroups are dealt round-robin to the 8 XCDs),
+// which keeps each weight tile in that XCD's L2 while it is reused.  Split-K
+// (chosen from N and K only, never from M) writes fp32 partials that a
+// second, LDS-free kernel adds in split order before the epilogue, so a
+// row's result never depends on how many rows there are.
 //
 // fp32 path: a 64x64 SIMT tile kernel (exact fp32 products, fp32 accumulate)
 // for the fp32 configuration.
@@ -30,9 +40,7 @@ namespace cb {
 namespace {
 
 // bf16 tiles
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8, CLD = BN + 4;
-constexpr int kGemmSmem = 2 * (BM + BN) * LDK * 2;  // 73728 B
-static_assert(BM * CLD * 4 <= kGemmSmem, "C tile must fit in the operand buffers");
+constexpr int BM = 128, BN = 128, BK = 64, CLD = BN + 4;
 // fp32 tiles
 constexpr int FBM = 64, FBN = 64, FBK = 16, FCLD = FBN + 4;
 
@@ -132,17 +140,17 @@ __device__ void epi_store(const EpiParams& e, int gm, int c, const float v[8]) {
   else store8((T*)e.out + (int64_t)gm * e.ld_out + c, v);
 }
 
-// Apply the epilogue to a bm x bn fp32 tile held in LDS (row stride cld).
-template <typename T, int bm, int bn, int NT>
+// Apply the epilogue KIND to a bm x bn fp32 tile held in LDS (row stride cld).
+template <typename T, int bm, int bn, int NT, int KIND>
 __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float* Cs, int cld, int m0, int tn,
                              int M, int N) {
-  const bool swiglu = e.kind == EPI_SWIGLU;
+  constexpr bool swiglu = KIND == EPI_SWIGLU;
   const int cols = swiglu ? bn / 2 : bn;
   const int tpr = cols / 8;  // threads per row (power of two, <= 64)
   const int rpp = NT / tpr;
   const int tid = threadIdx.x;
   const int lr = tid / tpr, lc = (tid % tpr) * 8;
-  const bool want_dev = e.kind == EPI_QKV && e.dev_part != nullptr;
+  const bool want_dev = KIND == EPI_QKV && e.dev_part != nullptr;
   const int q_end = e.q_dim, k_end = e.q_dim + e.kv_dim;
   const bool k_tile = want_dev && tn * bn < k_end && tn * bn + bn > q_end;
   for (int r0 = 0; r0 < bm; r0 += rpp) {
@@ -154,7 +162,7 @@ __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float*
       float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = row[lc + j];
-      if (swiglu) {
+      if constexpr (swiglu) {
         const int f = tn * (bn / 2) + lc;
         if (f < B.n_feat) {
           float u[8];
@@ -165,8 +173,8 @@ __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float*
       } else {
         const int c = tn * bn + lc;
         if (c < N) {
-          if (e.kind == EPI_QKV) contrib = epi_qkv<T>(e, gm, c, v);
-          else if (e.kind == EPI_RESID) epi_resid<T>(e, gm, c, v);
+          if constexpr (KIND == EPI_QKV) contrib = epi_qkv<T>(e, gm, c, v);
+          else if constexpr (KIND == EPI_RESID) epi_resid<T>(e, gm, c, v);
           else epi_store<T>(e, gm, c, v);
         }
       }
@@ -188,11 +196,45 @@ __device__ __forceinline__ int xcd_remap(int id, int nb) {
   return (nb & 7) == 0 ? (id & 7) * (nb >> 3) + (id >> 3) : id;
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, int ntiles) {
-  __shared__ __attribute__((aligned(16))) char smem[kGemmSmem];
-  bf16_t* As = (bf16_t*)smem;            // [2][BM][LDK]
-  bf16_t* Bs = As + 2 * BM * LDK;        // [2][BN][LDK]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// s_waitcnt vmcnt(n) lgkmcnt(0): this wave's LDS DMA up to the n most recent
+// loads has landed and its LDS reads have returned.
+#define CB_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
+// Workgroup barrier without a memory fence (a fence would drain the DMA ring);
+// the empty asm statements keep the compiler from moving LDS accesses across it.
+#define CB_BARRIER()                  \
+  do {                                \
+    asm volatile("" ::: "memory");    \
+    __builtin_amdgcn_s_barrier();     \
+    asm volatile("" ::: "memory");    \
+  } while (0)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at p (gfx9 layout: raw buffer, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Byte offset of 16-byte chunk c of row r in a swizzled [rows][BK] bf16 tile:
+// rows are 128 B, chunk c of row r sits in slot c ^ ((r >> 1) & 7), so the
+// 16 rows read by one fragment load cover all 64 banks exactly once.
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+#ifndef CB_GEMM_NSTAGE
+#define CB_GEMM_NSTAGE 3
+#endif
+#ifndef CB_GEMM_MINBLOCKS
+#define CB_GEMM_MINBLOCKS 1
+#endif
+constexpr int NSTAGE = CB_GEMM_NSTAGE;          // LDS ring depth (K steps in flight)
+constexpr int kStageBytes = (BM + BN) * BK * 2;  // 32 KB
+constexpr int kGemmSmem3 = NSTAGE * kStageBytes > BM * CLD * 4 ? NSTAGE * kStageBytes : BM * CLD * 4;
+
+template <int KIND>
+__global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmArgs g, int mt, int ntiles) {
+  __shared__ __attribute__((aligned(16))) char smem[kGemmSmem3];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = id % mt, tn = id / mt;
   const int m0 = tm * BM;
@@ -202,76 +244,74 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
   const int ke = min(K, kb + kchunk);
   const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
 
-  // Loader: each thread moves 4 A and 4 B chunks of 16 B per K step.  The
-  // addresses are always in bounds (invalid rows fall back to row 0 / the
-  // weight's first row, the K tail to the first chunk of this split) and the
-  // zero fill is applied when the chunk is written to LDS, so no loaded value
-  // is consumed before the MFMAs of the current step have been issued.
-  typedef __attribute__((address_space(1))) const u32x4_t guint4;
-  const guint4* ag[4];
-  const guint4* bg[4];
-  bool aok[4], bok[4];
-  int lrow[4], lcol[4];
+  // DMA plan: wave w moves row groups (w*4 + j)*8 .. +7 of the A and B tiles
+  // (j = 0..3); lane i of a group fills slot i%8 of row i/8 with the logical
+  // chunk slot ^ ((row >> 1) & 7).  Rows past the matrix and chunks past the
+  // K range are out of the buffer's range and load as zero.
+  const uint32_t kOOB = 0x80000000u;
+  __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
+  __amdgpu_buffer_rsrc_t rb[4];
+  uint32_t aoff[4], boff[4];
+  int lcol[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    lrow[i] = c >> 3;
-    lcol[i] = (c & 7) * 8;
-    aok[i] = m0 + lrow[i] < M;
-    ag[i] = (const guint4*)((const bf16_t*)g.A + (int64_t)(aok[i] ? m0 + lrow[i] : 0) * K);
-    const bf16_t* br = b_row<bf16_t>(g.B, K, g.N, tn, BN, lrow[i]);
-    bok[i] = br != nullptr;
-    bg[i] = (const guint4*)(bok[i] ? br : (const bf16_t*)g.B.p0);
+  for (int j = 0; j < 4; ++j) {
+    const int grp = w * 4 + j;
+    const int row = grp * 8 + (lane >> 3);
+    const int slot = lane & 7;
+    lcol[j] = (slot ^ ((row >> 1) & 7)) * 8;      // logical k offset of this lane's chunk
+    aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
+    // B: the 8 rows of a group always come from one weight matrix
+    const int r0 = grp * 8;
+    const void* base;
+    int brow, nrows;
+    if (g.B.mode == 0) {
+      const int c0 = tn * BN + r0;
+      if (c0 < g.B.n1) { base = g.B.p0; brow = c0; nrows = g.B.n1; }
+      else if (c0 < g.B.n2) { base = g.B.p1; brow = c0 - g.B.n1; nrows = g.B.n2 - g.B.n1; }
+      else { base = g.B.p2; brow = c0 - g.B.n2; nrows = g.N - g.B.n2; }
+    } else {
+      base = r0 < BN / 2 ? g.B.p0 : g.B.p1;
+      brow = tn * (BN / 2) + (r0 % (BN / 2));
+      nrows = g.B.n_feat;
+    }
+    rb[j] = make_rsrc(base, (uint32_t)((int64_t)(nrows > 0 ? nrows : 0) * K * 2));
+    const int myrow = brow + (lane >> 3);
+    boff[j] = myrow < nrows ? (uint32_t)((int64_t)myrow * K * 2) : kOOB;
   }
-  u32x4_t ra[4], rb[4];
-  const u32x4_t z4 = {0u, 0u, 0u, 0u};
+
+  auto issue = [&](int stage, int k0) {
+    char* sa = smem + stage * kStageBytes;
+    char* sb = sa + BM * BK * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int grp = w * 4 + j;
+      const int kk = k0 + lcol[j];
+      const bool kin = kk < ke;
+      const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
+      const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+    }
+  };
 
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  if (nk > 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kk = kb + lcol[i];
-      const int kc = (kk < ke ? kk : kb) >> 3;
-      ra[i] = ag[i][kc];
-      rb[i] = bg[i][kc];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool kin = kb + lcol[i] < ke;
-      *reinterpret_cast<u32x4_t*>(As + lrow[i] * LDK + lcol[i]) = (aok[i] && kin) ? ra[i] : z4;
-      *reinterpret_cast<u32x4_t*>(Bs + lrow[i] * LDK + lcol[i]) = (bok[i] && kin) ? rb[i] : z4;
-    }
-  }
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const int kn = kb + (it + 1) * BK;  // next K step
-    const bool more = it + 1 < nk;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = kn + lcol[i];
-        const int kc = (kk < ke ? kk : kb) >> 3;
-        ra[i] = ag[i][kc];
-        rb[i] = bg[i][kc];
-      }
-    }
-    const bf16_t* Ac = As + cur * BM * LDK;
-    const bf16_t* Bc = Bs + cur * BN * LDK;
+  const int fr = lane & 15, fc = lane >> 4;
+
+  auto compute = [&](int stage) {
+    const char* sa = smem + stage * kStageBytes;
+    const char* sb = sa + BM * BK * 2;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       bf16x8_t af[4], bfr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8_t*>(Ac + (wm + i * 16 + fr) * LDK + ks * 32 + fk);
-        bfr[i] = *reinterpret_cast<const bf16x8_t*>(Bc + (wn + i * 16 + fr) * LDK + ks * 32 + fk);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz(wm + i * 16 + fr, ks * 4 + fc));
+        bfr[i] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn + i * 16 + fr, ks * 4 + fc));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -279,18 +319,30 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      bf16_t* An = As + (cur ^ 1) * BM * LDK;
-      bf16_t* Bn = Bs + (cur ^ 1) * BN * LDK;
+  };
+
+  // prologue: NSTAGE-1 K steps in flight
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool kin = kn + lcol[i] < ke;
-        *reinterpret_cast<u32x4_t*>(An + lrow[i] * LDK + lcol[i]) = (aok[i] && kin) ? ra[i] : z4;
-        *reinterpret_cast<u32x4_t*>(Bn + lrow[i] * LDK + lcol[i]) = (bok[i] && kin) ? rb[i] : z4;
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < nk) issue(st, kb + st * BK);
+  // main loop, unrolled by the ring depth so every LDS address is static
+  for (int it0 = 0; it0 < nk; it0 += NSTAGE) {
+#pragma unroll
+    for (int u = 0; u < NSTAGE; ++u) {
+      const int it = it0 + u;
+      if (it < nk) {
+        // this wave's DMA for step `it` is done once at most the later
+        // steps' 8 loads per step are outstanding
+        if (it + 1 < nk) CB_WAIT_VMCNT(8 * (NSTAGE - 2));
+        else CB_WAIT_VMCNT(0);
+        CB_BARRIER();   // every wave's step `it` is in LDS; step it-1's buffer is free
+        if (it + NSTAGE - 1 < nk) issue((u + NSTAGE - 1) % NSTAGE, kb + (it + NSTAGE - 1) * BK);
+        compute(u);
       }
     }
-    __syncthreads();
   }
+  CB_WAIT_VMCNT(0);
+  __syncthreads();
 
   // accumulators -> fp32 tile in LDS.  Lane l of a 16x16 block holds column
   // l%16 and rows 4*(l/16) .. 4*(l/16)+3.
@@ -301,10 +353,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        Cs[(wm + i * 16 + (lane >> 4) * 4 + v) * CLD + wn + j * 16 + fr] = acc[i][j][v];
+        Cs[(wm + i * 16 + fc * 4 + v) * CLD + wn + j * 16 + fr] = acc[i][j][v];
   __syncthreads();
 
   if (g.splits > 1) {
+    // split-K partial; splitk_epilogue_kernel adds the splits in order
     const int ldp = ntiles * BN;
     float* P = g.part + (int64_t)blockIdx.y * M * ldp;
     for (int idx = tid; idx < BM * BN / 4; idx += 256) {
@@ -315,31 +368,198 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g, int mt, i
     }
     return;
   }
-  run_epilogue<bf16_t, BM, BN, 256>(g.epi, g.B, Cs, CLD, m0, tn, M, g.N);
+  run_epilogue<bf16_t, BM, BN, 256, KIND>(g.epi, g.B, Cs, CLD, m0, tn, M, g.N);
 }
 
-// Sum the split-K partials of one tile in split order, then run the epilogue.
-template <typename T, int bm, int bn>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int mt, int ntiles) {
-  __shared__ __attribute__((aligned(16))) float Cs[bm * (bn + 4)];
-  const int tid = threadIdx.x;
-  const int tm = blockIdx.x % mt, tn = blockIdx.x / mt;
-  const int m0 = tm * bm, M = g.M;
-  const int ldp = ntiles * bn;
-  for (int idx = tid; idx < bm * bn / 4; idx += 256) {
-    const int r = idx / (bn / 4), c4 = (idx % (bn / 4)) * 4;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (m0 + r < M) {
-      for (int sp = 0; sp < g.splits; ++sp) {
-        const float4 p =
-            *reinterpret_cast<const float4*>(g.part + ((int64_t)sp * M + m0 + r) * ldp + tn * bn + c4);
-        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel, large tile: 256x256 output, 4 waves of 128x128 (8x8 MFMA
+// blocks, accumulators in AGPRs), K step 32 with a 4-deep LDS ring.  Each
+// wave does 64 MFMAs per barrier, four times the 128x128 kernel, so the
+// per-step fixed costs (barrier, first LDS latency, waits) are amortised over
+// more matrix work.  Used where N is large (the gate/up projection).
+// ---------------------------------------------------------------------------
+constexpr int LBM = 256, LBN = 256, LBK = 32, LNS = 4, LCLD = LBN + 4;
+constexpr int kLStage = (LBM + LBN) * LBK * 2;                         // 32 KB
+constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LCLD * 4;
+
+// 64-byte rows (BK = 32): chunk c (0..3) of row r sits in slot c ^ ((r >> 2) & 3);
+// the 16 rows of one fragment load then cover all 64 banks once.
+__device__ __forceinline__ int swz32(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int mt, int ntiles) {
+  __shared__ __attribute__((aligned(16))) char smem[kLSmem];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = id % mt, tn = id / mt;
+  const int m0 = tm * LBM;
+  const int M = g.M, K = g.K;
+  const int nk = (K + LBK - 1) / LBK;
+
+  // DMA plan: a wave instruction fills 16 rows x 64 B; wave w moves row
+  // groups w*4 + j (j = 0..3) of A and of B.
+  const uint32_t kOOB = 0x80000000u;
+  __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
+  __amdgpu_buffer_rsrc_t rb[4];
+  uint32_t aoff[4], boff[4];
+  int lcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int grp = w * 4 + j;
+    const int row = grp * 16 + (lane >> 2);
+    lcol[j] = ((lane & 3) ^ ((row >> 2) & 3)) * 8;
+    aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
+    const int r0 = grp * 16;
+    const void* base;
+    int brow, nrows;
+    if (g.B.mode == 0) {
+      const int c0 = tn * LBN + r0;
+      if (c0 < g.B.n1) { base = g.B.p0; brow = c0; nrows = g.B.n1; }
+      else if (c0 < g.B.n2) { base = g.B.p1; brow = c0 - g.B.n1; nrows = g.B.n2 - g.B.n1; }
+      else { base = g.B.p2; brow = c0 - g.B.n2; nrows = g.N - g.B.n2; }
+    } else {
+      base = r0 < LBN / 2 ? g.B.p0 : g.B.p1;
+      brow = tn * (LBN / 2) + (r0 % (LBN / 2));
+      nrows = g.B.n_feat;
+    }
+    rb[j] = make_rsrc(base, (uint32_t)((int64_t)(nrows > 0 ? nrows : 0) * K * 2));
+    const int myrow = brow + (lane >> 2);
+    boff[j] = myrow < nrows ? (uint32_t)((int64_t)myrow * K * 2) : kOOB;
+  }
+  auto issue = [&](int stage, int k0) {
+    char* sa = smem + stage * kLStage;
+    char* sb = sa + LBM * LBK * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int grp = w * 4 + j;
+      const int kk = k0 + lcol[j];
+      const bool kin = kk < K;
+      const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
+      const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const int fr = lane & 15, fc = lane >> 4;
+  auto compute = [&](int stage) {
+    const char* sa = smem + stage * kLStage;
+    const char* sb = sa + LBM * LBK * 2;
+    bf16x8_t af[8], bfr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
+      bfr[i] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + i * 16 + fr, fc));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int st = 0; st < LNS - 1; ++st)
+    if (st < nk) issue(st, st * LBK);
+  for (int it0 = 0; it0 < nk; it0 += LNS) {
+#pragma unroll
+    for (int u = 0; u < LNS; ++u) {
+      const int it = it0 + u;
+      if (it < nk) {
+        // this wave's step `it` landed once at most the later steps' loads
+        // (8 per step) are outstanding
+        const int later = min(nk - 1 - it, LNS - 2);
+        if (later >= 2) CB_WAIT_VMCNT(16);
+        else if (later == 1) CB_WAIT_VMCNT(8);
+        else CB_WAIT_VMCNT(0);
+        CB_BARRIER();
+        if (it + LNS - 1 < nk) issue((u + LNS - 1) % LNS, (it + LNS - 1) * LBK);
+        compute(u);
       }
     }
-    *reinterpret_cast<float4*>(Cs + r * (bn + 4) + c4) = s;
   }
+  CB_WAIT_VMCNT(0);
   __syncthreads();
-  run_epilogue<T, bm, bn, 256>(g.epi, g.B, Cs, bn + 4, m0, tn, M, g.N);
+
+  // epilogue in two halves of 128 rows (the fp32 tile of 256 rows does not fit)
+  float* Cs = (float*)smem;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((w >> 1) == half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Cs[(i * 16 + fc * 4 + v) * LCLD + wn + j * 16 + fr] = acc[i][j][v];
+    }
+    __syncthreads();
+    run_epilogue<bf16_t, 128, LBN, 256, KIND>(g.epi, g.B, Cs, LCLD, m0 + half * 128, tn, M, g.N);
+    __syncthreads();
+  }
+}
+
+// Split-K finish: one thread per 8 output columns of a row adds the split
+// partials in split order straight from memory and applies the epilogue.
+// 16 rows x one 128-column tile per workgroup; no LDS staging.
+template <int KIND>
+__device__ __forceinline__ float sum8(const GemmArgs& g, int ldp, int gm, int col, float v[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  for (int sp = 0; sp < g.splits; ++sp) {
+    const float* p = g.part + ((int64_t)sp * g.M + gm) * ldp + col;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  return 0.f;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, int ntiles) {
+  const int tn = blockIdx.y;
+  const int ldp = ntiles * BN;
+  const int tid = threadIdx.x;
+  const EpiParams& e = g.epi;
+  constexpr bool swiglu = KIND == EPI_SWIGLU;
+  constexpr int cols = swiglu ? BN / 2 : BN;
+  constexpr int tpr = cols / 8;
+  constexpr int rpb = 256 / tpr;
+  const int r = blockIdx.x * rpb + tid / tpr;
+  const int lc = (tid % tpr) * 8;
+  const int gm = r;
+  const bool k_tile = KIND == EPI_QKV && e.dev_part != nullptr && tn * BN < e.q_dim + e.kv_dim &&
+                      tn * BN + BN > e.q_dim;
+  float contrib = 0.f;
+  if (gm < g.M) {
+    float v[8];
+    sum8<KIND>(g, ldp, gm, tn * BN + lc, v);
+    if constexpr (swiglu) {
+      float u[8];
+      sum8<KIND>(g, ldp, gm, tn * BN + BN / 2 + lc, u);
+      const int f = tn * (BN / 2) + lc;
+      if (f < g.B.n_feat) epi_swiglu<bf16_t>(e, gm, f, v, u);
+    } else {
+      const int c = tn * BN + lc;
+      if (c < g.N) {
+        if constexpr (KIND == EPI_QKV) contrib = epi_qkv<bf16_t>(e, gm, c, v);
+        else if constexpr (KIND == EPI_RESID) epi_resid<bf16_t>(e, gm, c, v);
+        else epi_store<bf16_t>(e, gm, c, v);
+      }
+    }
+  }
+  if (k_tile) {
+    for (int o = tpr / 2; o > 0; o >>= 1) contrib += __shfl_xor(contrib, o);
+    if ((tid % tpr) == 0 && gm < g.M) e.dev_part[(int64_t)(tn - e.k_tile0) * g.M + gm] = contrib;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -395,12 +615,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, int mt, int n
 #pragma unroll
     for (int j = 0; j < 4; ++j) Cs[(ty * 4 + i) * FCLD + tx * 4 + j] = acc[i][j];
   __syncthreads();
-  run_epilogue<float, FBM, FBN, 256>(g.epi, g.B, Cs, FCLD, m0, tn, M, g.N);
+  switch (g.epi.kind) {
+    case EPI_QKV: run_epilogue<float, FBM, FBN, 256, EPI_QKV>(g.epi, g.B, Cs, FCLD, m0, tn, M, g.N); break;
+    case EPI_RESID: run_epilogue<float, FBM, FBN, 256, EPI_RESID>(g.epi, g.B, Cs, FCLD, m0, tn, M, g.N); break;
+    case EPI_SWIGLU: run_epilogue<float, FBM, FBN, 256, EPI_SWIGLU>(g.epi, g.B, Cs, FCLD, m0, tn, M, g.N); break;
+    default: run_epilogue<float, FBM, FBN, 256, EPI_STORE>(g.epi, g.B, Cs, FCLD, m0, tn, M, g.N); break;
+  }
 }
 
 }  // namespace
 
 int gemm_bn(int dtype) { return dtype == CB_BF16 ? BN : FBN; }
+
+
 
 int gemm_n_tiles(int dtype, const BOperand& B, int N) {
   const int bn = gemm_bn(dtype);
@@ -418,19 +645,43 @@ int gemm_splits(int dtype, int n_tiles, int K) {
 hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
   if (g0.M <= 0) return hipSuccess;
   GemmArgs g = g0;
+  if (dtype == CB_BF16 && g.B.mode == 1) {
+    // gated pair (gate/up): 256x256 tiles, no split
+    const int nt = (g.B.n_feat + LBN / 2 - 1) / (LBN / 2);
+    const int mt = (g.M + LBM - 1) / LBM;
+    g.N = nt * LBN;
+    g.splits = 1;
+    LaunchScope ls("gemm_gateup", s);
+    gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), 256, 0, s>>>(g, mt, nt);
+    return hipGetLastError();
+  }
   const int ntiles = gemm_n_tiles(dtype, g.B, g.N);
   if (g.B.mode == 1) g.N = ntiles * gemm_bn(dtype);
   if (dtype == CB_BF16) {
     const int mt = (g.M + BM - 1) / BM;
+    const dim3 grid(mt * ntiles, g.splits);
+    const char* name = g.epi.kind == EPI_QKV ? "gemm_qkv" : g.epi.kind == EPI_SWIGLU ? "gemm_gateup"
+                       : g.epi.kind == EPI_RESID && g.epi.out_f32 ? "gemm_o" : "gemm_down";
     {
-      LaunchScope ls(g.epi.kind == EPI_QKV ? "gemm_qkv" : g.epi.kind == EPI_SWIGLU ? "gemm_gateup"
-                     : g.epi.kind == EPI_RESID && g.epi.out_f32 ? "gemm_o" : "gemm_down", s);
-      gemm_bf16_kernel<<<dim3(mt * ntiles, g.splits), dim3(256), 0, s>>>(g, mt, ntiles);
+      LaunchScope ls(name, s);
+      switch (g.epi.kind) {
+        case EPI_QKV: gemm_bf16_kernel<EPI_QKV><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
+        case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
+        case EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
+        default: gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.splits <= 1) return e;
-    LaunchScope ls("splitk_reduce", s);
-    splitk_reduce_kernel<bf16_t, BM, BN><<<dim3(mt * ntiles), dim3(256), 0, s>>>(g, mt, ntiles);
+    const int tpr = (g.epi.kind == EPI_SWIGLU ? BN / 2 : BN) / 8;
+    const dim3 rgrid((g.M + 256 / tpr - 1) / (256 / tpr), ntiles);
+    LaunchScope ls("splitk_epilogue", s);
+    switch (g.epi.kind) {
+      case EPI_QKV: splitk_epilogue_kernel<EPI_QKV><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+      case EPI_RESID: splitk_epilogue_kernel<EPI_RESID><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+      case EPI_SWIGLU: splitk_epilogue_kernel<EPI_SWIGLU><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+      default: splitk_epilogue_kernel<EPI_STORE><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+    }
     return hipGetLastError();
   }
   const int mt = (g.M + FBM - 1) / FBM;

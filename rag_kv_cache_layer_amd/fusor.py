@@ -18,7 +18,8 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libcacheblend.so")
+# CB_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("CB_LIB") or os.path.join(PKG, "libcacheblend.so")
 
 CB_F32, CB_BF16 = 0, 1
 _STATUS = {0: "CB_OK", 1: "CB_ERR_ARG", 2: "CB_ERR_SHAPE", 3: "CB_ERR_INDEX", 4: "CB_ERR_WORKSPACE",
@@ -295,3 +296,44 @@ def full_prefill_layer(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, h
                                        _dptr(k_out, "k_out", dt, T * kv), _dptr(v_out, "v_out", dt, T * kv),
                                        _dptr(hidden_out, "hidden_out", dt, T * d), _dptr(ws, "ws", _torch().uint8),
                                        ws.numel(), _stream(stream)), "cb_full_prefill_layer")
+
+
+# ---------------------------------------------------------------------------
+# stack driver (gradual filtering across layers)
+# ---------------------------------------------------------------------------
+
+def blend_stack(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: DeviceRope, k_caches, v_caches, T: int,
+                chunk_offsets: Sequence[int], x_first, ks: Sequence[int], ws, stream=None, shift: bool = True):
+    """Run the fusor through every layer (CacheBlend section 4.3, Figure 9).
+
+    k_caches, v_caches: device [n_layers][T][n_kv][hd], each chunk's cached K/V
+    in context order (keys at their local positions when shift=True, the
+    re-alignment then runs once over all layers).  x_first: device [m0][d],
+    the first layer's input for rows first_chunk_len .. T-1.  ks: per-layer
+    k_out (filter_schedule).  Layer 0 recomputes every candidate; later layers
+    recompute the rows the previous layer kept.  Every row count is known on
+    the host, so nothing waits on the device.  Returns a list of per-layer
+    dicts (s_in, dev, s_out, y) of device tensors; the last y holds the output
+    of the rows the last layer kept."""
+    torch = _torch()
+    n_layers = len(layers)
+    offs = [int(o) for o in chunk_offsets]
+    n_ctx, L0 = offs[-1], offs[1] if len(offs) > 1 else offs[-1]
+    kv = cfg.n_kv_heads * cfg.head_dim
+    if shift:
+        rope_shift(cfg, rope, k_caches, T * kv, n_layers, T, offs, stream)
+    dev_ = x_first.device
+    s = torch.arange(L0, T, dtype=torch.int32, device=dev_)
+    x = x_first
+    out = []
+    for l in range(n_layers):
+        m_in = s.numel()
+        m_out = expected_m_out(T, n_ctx, m_in, ks[l])
+        y = torch.empty((m_out, cfg.d_model), dtype=torch_dtype(cfg), device=dev_)
+        s_out = torch.empty(m_out, dtype=torch.int32, device=dev_)
+        dv = torch.empty(m_in, dtype=torch.float32, device=dev_)
+        blend_layer(cfg, layers[l], rope, k_caches[l], v_caches[l], T, n_ctx, L0, s, m_in, x, None, ks[l], y, dv,
+                    s_out, ws, stream)
+        out.append({"s_in": s, "dev": dv, "s_out": s_out, "y": y})
+        s, x = s_out, y
+    return out

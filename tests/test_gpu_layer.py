@@ -24,8 +24,10 @@ MED64 = synth.scaled(synth.PRESETS["llama8b_layer"], 1024, 16, 4, 64, 2776, [100
 MED128 = synth.scaled(synth.PRESETS["llama70b_stack"], 1024, 8, 1, 128, 2048, [130, 61, 140], 9, n_layers=1)
 # fp32 with GQA and ragged chunks
 F32GQA = synth.scaled(synth.PRESETS["llama8b_layer"], 128, 8, 2, 16, 344, [24, 20, 28], 8).with_(dtype="f32")
-CASES = [TINY, F32GQA, MED64, MED128]
-IDS = ["tiny_f32", "f32_gqa", "bf16_hd64", "bf16_hd128"]
+# bf16, keys past 512: the attention key split and its merge are exercised
+LONG = synth.scaled(synth.PRESETS["llama8b_layer"], 512, 8, 2, 64, 1024, [300, 400, 500], 20)
+CASES = [TINY, F32GQA, MED64, MED128, LONG]
+IDS = ["tiny_f32", "f32_gqa", "bf16_hd64", "bf16_hd128", "bf16_long"]
 
 
 class Gpu:
@@ -83,7 +85,7 @@ def test_full_prefill(p):
     assert rel_err(k2, kw2) < tol and rel_err(y2, yw2) < tol
 
 
-@pytest.mark.parametrize("p", [TINY, MED64], ids=["tiny_f32", "bf16_hd64"])
+@pytest.mark.parametrize("p", [TINY, MED64, LONG], ids=["tiny_f32", "bf16_hd64", "bf16_long"])
 def test_prefix_invariant_bit_exact(p):
     """The first chunk's K/V and outputs from a prefill of that chunk alone
     equal those rows of the full-context prefill bit for bit (prefix caching:
