@@ -164,7 +164,7 @@ Ws layout(const cb_layer_config& c, int m, int T) {
   w.u = take(M * D.F * D.b);
   w.part = take(part_floats(c.dtype, D, (int)M) * 4);
   // attention key-split partials: only for row counts that use the split
-  const size_t arows = std::min(M, attn_part_rows(c.n_kv_heads));
+  const size_t arows = std::min(M, attn_part_rows(c.n_q_heads, c.n_kv_heads));
   const size_t nsplit = c.dtype == CB_BF16 ? (size_t)(std::max(T, 1) + 511) / 512 : 0;
   w.o_part = take(nsplit * arows * D.q_dim * 4);
   w.ml_part = take(nsplit * arows * c.n_q_heads * 8);
@@ -550,7 +550,7 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   aa.n_q = cfg->n_q_heads;
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
-  aa.key_split = attn_key_split(dt, m_out, cfg->n_kv_heads);
+  aa.key_split = attn_key_split(dt, m_out, cfg->n_q_heads, cfg->n_kv_heads);
   aa.o_part = at<float>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
@@ -602,7 +602,7 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   aa.n_q = cfg->n_q_heads;
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
-  aa.key_split = attn_key_split(dt, T, cfg->n_kv_heads);
+  aa.key_split = attn_key_split(dt, T, cfg->n_q_heads, cfg->n_kv_heads);
   aa.o_part = at<float>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));

@@ -102,19 +102,25 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
   const bf16_t* Kg = (const bf16_t*)a.K + kvh * HD;
   const bf16_t* Vg = (const bf16_t*)a.V + kvh * HD;
 
-  // staging: unit u = (key group kg of 4 keys, dim chunk dc of 8 dims)
+  // staging: each thread moves 4 consecutive keys x 8 dims of K and of V.
+  // For K the dim chunk varies fastest across lanes, so 16 lanes write one
+  // key row contiguously (conflict-free LDS stores); for V the key group
+  // varies fastest, which suits its transposed 8-byte stores.  Threads past
+  // the last unit load a valid duplicate and never store it, so the loads
+  // carry no branch.
   u32x4_t rk[UPT][4], rv[UPT][4];
-  // threads past the last unit load a valid duplicate and never store it,
-  // so the loads carry no branch
 #define CB_ATTN_FETCH(T0)                                                  \
   _Pragma("unroll") for (int j = 0; j < UPT; ++j) {                        \
     const int u = min(tid + j * NT, UNITS - 1);                            \
+    const int kgk = u / (HD / 8), dck = u % (HD / 8);                      \
     const int kg = u % (KT / 4), dc = u / (KT / 4);                        \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                        \
-      int t = (T0) + kg * 4 + r;                                           \
+      int t = (T0) + kgk * 4 + r;                                          \
       t = t < a.T ? t : a.T - 1; /* keys past T are masked below */       \
-      rk[j][r] = *(const gvec*)(Kg + (int64_t)t * ldkv + dc * 8);          \
-      rv[j][r] = *(const gvec*)(Vg + (int64_t)t * ldkv + dc * 8);          \
+      rk[j][r] = *(const gvec*)(Kg + (int64_t)t * ldkv + dck * 8);         \
+      int tv = (T0) + kg * 4 + r;                                          \
+      tv = tv < a.T ? tv : a.T - 1;                                        \
+      rv[j][r] = *(const gvec*)(Vg + (int64_t)tv * ldkv + dc * 8);         \
     }                                                                      \
   }
 
@@ -125,9 +131,10 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
     for (int j = 0; j < UPT; ++j) {
       const int u = tid + j * NT;
       if (UNITS % NT != 0 && u >= UNITS) continue;
-      const int kg = u % (KT / 4), dc = u / (KT / 4);
+      const int kgk = u / (HD / 8), dck = u % (HD / 8);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x4_t*)(Ks + (kg * 4 + r) * KLD + dc * 8) = rk[j][r];
+      for (int r = 0; r < 4; ++r) *(u32x4_t*)(Ks + (kgk * 4 + r) * KLD + dck * 8) = rk[j][r];
+      const int kg = u % (KT / 4), dc = u / (KT / 4);
       // V^T: dims dc*8 .. +7, keys kg*4 .. +3 as one 8-byte store per dim
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -153,7 +160,13 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
         s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
       }
     }
+    // online softmax per query, in base-2 units (x = s * scale_log2, one
+    // fused multiply-add inside the exponent); the output accumulators are
+    // rescaled only when some query's running max grew -- otherwise alpha is
+    // exactly 1 for every lane and the multiply is skipped
     bf16x8_t pb[2][2];
+    bool grew = false;
+    float alpha[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       float mx = -INFINITY;
@@ -162,30 +175,29 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int key = t0 + kb * 16 + 4 * gp + v;
-          const float x = key <= pos[b] ? s[b][kb][v] * scale_log2 : -INFINITY;
+          const float x = key <= pos[b] ? s[b][kb][v] : -INFINITY;
           s[b][kb][v] = x;
           mx = fmaxf(mx, x);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[b], mx);
+      const float m_new = fmaxf(m_run[b], mx * scale_log2);
+      grew |= m_new > m_run[b];
       const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
-      const float alpha = exp2f(m_run[b] - m_use);
+      alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use);
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float e = exp2f(s[b][kb][v] - m_use);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][kb][v], scale_log2, -m_use));
           s[b][kb][v] = e;
           sum += e;
         }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
-      l_run[b] = l_run[b] * alpha + sum;
+      l_run[b] = l_run[b] * alpha[b] + sum;
       m_run[b] = m_new;
-#pragma unroll
-      for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha;
       // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j
       // (j<4) or 32st+16+4gp+(j-4), matching the V^T reads below
 #pragma unroll
@@ -195,6 +207,12 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
           pb[b][st][v] = (__bf16)s[b][2 * st][v];
           pb[b][st][4 + v] = (__bf16)s[b][2 * st + 1][v];
         }
+    }
+    if (__any(grew)) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha[b];
     }
 #pragma unroll
     for (int mb = 0; mb < HD / 16; ++mb)
@@ -242,13 +260,16 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 // Merge the key-split partials of one row in split order, for every head:
 // out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s over the splits that
 // hold keys of the row.  Rows of tiles that were not split are skipped.  One
-// workgroup per row; each thread owns 4 consecutive dims of one head.
+// workgroup per row: the per-(head, split) weights go to LDS first, then each
+// thread adds the splits of 4 consecutive dims of one head with independent
+// loads.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  extern __shared__ float coef[];   // [n_q][ns]
   __shared__ int s_pm;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  const int tile = i / kRowTile;
+  const int tile = i / kRowTile;   // workgroups of the attention kernel cover kRowTile rows
   if (tid < 64) {
     const int r = tile * kRowTile + tid;
     int p = 0;
@@ -265,24 +286,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   int p = a.qpos ? a.qpos[i] : i;
   p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
   const int ns = p / a.key_split + 1;
-  const int per_row = a.n_q * HD;
-  for (int c = tid * 4; c < per_row; c += 256 * 4) {
-    const int head = c / HD;
+  for (int head = tid; head < a.n_q; head += 256) {
     float m = -INFINITY;
     for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, a.ml_part[(((int64_t)sp * a.m + i) * a.n_q + head) * 2]);
     float den = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + (((int64_t)sp * a.m + i) * a.n_q + head) * 2);
+      const float wgt = exp2f(ml.x - m);
+      coef[head * ns + sp] = wgt;
+      den += wgt * ml.y;
+    }
+    const float inv = 1.0f / den;
+    for (int sp = 0; sp < ns; ++sp) coef[head * ns + sp] *= inv;
+  }
+  __syncthreads();
+  const int per_row = a.n_q * HD;
+  for (int c = tid * 4; c < per_row; c += 256 * 4) {
+    const int head = c / HD;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sp = 0; sp < ns; ++sp) {
       const int64_t slot = ((int64_t)sp * a.m + i) * a.n_q + head;
-      const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
-      const float wgt = exp2f(ml.x - m);
-      den += wgt * ml.y;
+      const float wgt = coef[head * ns + sp];
       const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + (c % HD));
       num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;
     }
     bf16_t* Op = (bf16_t*)a.O + (int64_t)i * per_row + c;
-    const uint32_t w0 = (uint32_t)f2bf(num.x / den) | ((uint32_t)f2bf(num.y / den) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(num.z / den) | ((uint32_t)f2bf(num.w / den) << 16);
+    const uint32_t w0 = (uint32_t)f2bf(num.x) | ((uint32_t)f2bf(num.y) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(num.z) | ((uint32_t)f2bf(num.w) << 16);
     *reinterpret_cast<uint2*>(Op) = make_uint2(w0, w1);
   }
 }
@@ -348,19 +378,24 @@ hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.key_split <= 0) return e;
   LaunchScope ls("attn_merge", s);
-  attn_merge_kernel<HD><<<a.m, 256, 0, s>>>(a);
+  const size_t coef_bytes = (size_t)a.n_q * n_split * sizeof(float);
+  attn_merge_kernel<HD><<<a.m, 256, coef_bytes, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_key_split(int dtype, int m, int n_kv) {
+int attn_key_split(int dtype, int m, int n_q, int n_kv) {
+  (void)n_q;
   if (dtype != CB_BF16) return 0;
   const int blocks = (m + kRowTile - 1) / kRowTile * n_kv;
   return blocks < 512 ? kKeySplit : 0;
 }
 
-size_t attn_part_rows(int n_kv) { return (size_t)kRowTile * ((512 + n_kv - 1) / n_kv); }
+size_t attn_part_rows(int n_q, int n_kv) {
+  (void)n_q;
+  return (size_t)kRowTile * ((512 + n_kv - 1) / n_kv);
+}
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
   if (a.m <= 0) return hipSuccess;

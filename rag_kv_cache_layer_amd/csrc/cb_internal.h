@@ -196,8 +196,8 @@ struct AttnArgs {
 };
 // Key-split length used for m query rows (0 = none); chosen from the row and
 // head counts only.  attn_part_rows bounds the m for which it is non-zero.
-int attn_key_split(int dtype, int m, int n_kv);
-size_t attn_part_rows(int n_kv);
+int attn_key_split(int dtype, int m, int n_q, int n_kv);
+size_t attn_part_rows(int n_q, int n_kv);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
 }  // namespace cb

@@ -372,13 +372,16 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, large tile: 256x256 output, 4 waves of 128x128 (8x8 MFMA
-// blocks, accumulators in AGPRs), K step 32 with a 4-deep LDS ring.  Each
-// wave does 64 MFMAs per barrier, four times the 128x128 kernel, so the
-// per-step fixed costs (barrier, first LDS latency, waits) are amortised over
-// more matrix work.  Used where N is large (the gate/up projection).
+// bf16 MFMA kernel, large tile: 256x256 output, 8 waves of 128x64 (8x4 MFMA
+// blocks, accumulators in AGPRs, two waves per SIMD), K step 32 with a
+// 4-deep LDS ring.  The tile halves the L2-to-LDS bytes per flop of the
+// 128x128 kernel and each SIMD interleaves two waves' MFMA streams.  Used
+// where N is large (the gate/up projection).
 // ---------------------------------------------------------------------------
-constexpr int LBM = 256, LBN = 256, LBK = 32, LNS = 4, LCLD = LBN + 4;
+#ifndef CB_BIG_NSTAGE
+#define CB_BIG_NSTAGE 4
+#endif
+constexpr int LBM = 256, LBN = 256, LBK = 32, LNS = CB_BIG_NSTAGE, LCLD = LBN + 4;
 constexpr int kLStage = (LBM + LBN) * LBK * 2;                         // 32 KB
 constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LCLD * 4;
 
@@ -387,10 +390,10 @@ constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LC
 __device__ __forceinline__ int swz32(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
 template <int KIND>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int mt, int ntiles) {
+__global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int mt, int ntiles) {
   __shared__ __attribute__((aligned(16))) char smem[kLSmem];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // 8 waves: 2 (M) x 4 (N)
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = id % mt, tn = id / mt;
   const int m0 = tm * LBM;
@@ -398,15 +401,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
   const int nk = (K + LBK - 1) / LBK;
 
   // DMA plan: a wave instruction fills 16 rows x 64 B; wave w moves row
-  // groups w*4 + j (j = 0..3) of A and of B.
+  // groups w*2 + j (j = 0, 1) of A and of B (16 groups each per step).
   const uint32_t kOOB = 0x80000000u;
   __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
-  __amdgpu_buffer_rsrc_t rb[4];
-  uint32_t aoff[4], boff[4];
-  int lcol[4];
+  __amdgpu_buffer_rsrc_t rb[2];
+  uint32_t aoff[2], boff[2];
+  int lcol[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int grp = w * 4 + j;
+  for (int j = 0; j < 2; ++j) {
+    const int grp = w * 2 + j;
     const int row = grp * 16 + (lane >> 2);
     lcol[j] = ((lane & 3) ^ ((row >> 2) & 3)) * 8;
     aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
@@ -431,8 +434,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
     char* sa = smem + stage * kLStage;
     char* sb = sa + LBM * LBK * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int grp = w * 4 + j;
+    for (int j = 0; j < 2; ++j) {
+      const int grp = w * 2 + j;
       const int kk = k0 + lcol[j];
       const bool kin = kk < K;
       const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
@@ -442,26 +445,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
     }
   };
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = (w >> 2) * 128, wn = (w & 3) * 64;
   const int fr = lane & 15, fc = lane >> 4;
   auto compute = [&](int stage) {
     const char* sa = smem + stage * kLStage;
     const char* sb = sa + LBM * LBK * 2;
-    bf16x8_t af[8], bfr[8];
+    bf16x8_t af[8], bfr[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
-      bfr[i] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + i * 16 + fr, fc));
-    }
+    for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + j * 16 + fr, fc));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
@@ -474,10 +476,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
       const int it = it0 + u;
       if (it < nk) {
         // this wave's step `it` landed once at most the later steps' loads
-        // (8 per step) are outstanding
+        // (4 per step) are outstanding
         const int later = min(nk - 1 - it, LNS - 2);
-        if (later >= 2) CB_WAIT_VMCNT(16);
-        else if (later == 1) CB_WAIT_VMCNT(8);
+        if (later >= 3) CB_WAIT_VMCNT(12);
+        else if (later == 2) CB_WAIT_VMCNT(8);
+        else if (later == 1) CB_WAIT_VMCNT(4);
         else CB_WAIT_VMCNT(0);
         CB_BARRIER();
         if (it + LNS - 1 < nk) issue((u + LNS - 1) % LNS, (it + LNS - 1) * LBK);
@@ -492,16 +495,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
   float* Cs = (float*)smem;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if ((w >> 1) == half) {
+    if ((w >> 2) == half) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) Cs[(i * 16 + fc * 4 + v) * LCLD + wn + j * 16 + fr] = acc[i][j][v];
     }
     __syncthreads();
-    run_epilogue<bf16_t, 128, LBN, 256, KIND>(g.epi, g.B, Cs, LCLD, m0 + half * 128, tn, M, g.N);
+    run_epilogue<bf16_t, 128, LBN, 512, KIND>(g.epi, g.B, Cs, LCLD, m0 + half * 128, tn, M, g.N);
     __syncthreads();
   }
 }
@@ -652,7 +655,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
     g.N = nt * LBN;
     g.splits = 1;
     LaunchScope ls("gemm_gateup", s);
-    gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), 256, 0, s>>>(g, mt, nt);
+    gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), 512, 0, s>>>(g, mt, nt);
     return hipGetLastError();
   }
   const int ntiles = gemm_n_tiles(dtype, g.B, g.N);
