@@ -53,10 +53,27 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
   __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VLD];
   typedef __attribute__((address_space(1))) const u32x4_t gvec;
 
+  // 1-D grid over (group = KV head + n_kv * key split, row tile).  Workgroups
+  // are dealt round-robin to the 8 XCDs, each with its own L2; when the group
+  // count is a multiple of 8, workgroup b runs group b % 8 + 8 j on XCD b % 8,
+  // so every row tile that reads one group's K/V shares an L2 and the XCDs
+  // get equal mixes of key splits.  Latest row tiles (longest key ranges)
+  // come first within a group.
   const int n_tiles = (a.m + kRowTile - 1) / kRowTile;
-  const int tile = n_tiles - 1 - (int)blockIdx.x;   // latest positions (longest key ranges) first
-  const int kvh = blockIdx.y;
-  const int split = blockIdx.z;
+  const int n_groups = (int)gridDim.x / n_tiles;
+  const int b = blockIdx.x;
+  int grp, t;
+  if ((n_groups & 7) == 0) {
+    const int j = b >> 3;
+    grp = (b & 7) + 8 * (j / n_tiles);
+    t = j % n_tiles;
+  } else {
+    grp = b / n_tiles;
+    t = b % n_tiles;
+  }
+  const int tile = n_tiles - 1 - t;
+  const int kvh = grp % a.n_kv;
+  const int split = grp / a.n_kv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = kvh * G + w;
   const int q = lane & 15, gp = lane >> 4;
@@ -364,7 +381,7 @@ template <int HD>
 hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
   const int g = a.n_q / a.n_kv;
   const int n_split = a.key_split > 0 ? (a.T + a.key_split - 1) / a.key_split : 1;
-  const dim3 grid((a.m + kRowTile - 1) / kRowTile, a.n_kv, n_split);
+  const dim3 grid((a.m + kRowTile - 1) / kRowTile * a.n_kv * n_split);
   {
     LaunchScope ls("attention", s);
     switch (g) {

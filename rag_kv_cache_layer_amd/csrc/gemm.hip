@@ -378,16 +378,39 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
 // 128x128 kernel and each SIMD interleaves two waves' MFMA streams.  Used
 // where N is large (the gate/up projection).
 // ---------------------------------------------------------------------------
-#ifndef CB_BIG_NSTAGE
-#define CB_BIG_NSTAGE 4
+#ifndef CB_BIG_BK
+#define CB_BIG_BK 32
 #endif
-constexpr int LBM = 256, LBN = 256, LBK = 32, LNS = CB_BIG_NSTAGE, LCLD = LBN + 4;
-constexpr int kLStage = (LBM + LBN) * LBK * 2;                         // 32 KB
+#ifndef CB_BIG_NSTAGE
+#define CB_BIG_NSTAGE (CB_BIG_BK == 32 ? 4 : 2)
+#endif
+#ifndef CB_BIG_ILV
+#define CB_BIG_ILV 1
+#endif
+#ifndef CB_BIG_ILV_PER
+#define CB_BIG_ILV_PER 0   // MFMA rows between DMA groups (0: spread over the step)
+#endif
+constexpr int LBM = 256, LBN = 256, LBK = CB_BIG_BK, LNS = CB_BIG_NSTAGE, LCLD = LBN + 4;
+constexpr int kLStage = (LBM + LBN) * LBK * 2;                         // 32 or 64 KB
 constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LCLD * 4;
+static_assert(LBK == 32 || LBK == 64, "big tile: BK is 32 or 64");
+constexpr int kLRows = 1024 / (LBK * 2);       // rows one DMA instruction fills
+constexpr int kLGroups = LBM / kLRows / 8;     // row groups per operand per wave
 
-// 64-byte rows (BK = 32): chunk c (0..3) of row r sits in slot c ^ ((r >> 2) & 3);
-// the 16 rows of one fragment load then cover all 64 banks once.
-__device__ __forceinline__ int swz32(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// 64-byte rows (BK = 32) in 1 KB blocks of 16 rows.  Inside a block, row r
+// sits in row slot rho(r) and its 16-byte chunk c in slot c ^ ((r >> 1) & 3).
+// A fragment load (rows r = 0..15 of a block, chunk = lane / 16) then lands
+// on the same 16-byte bank groups, lane by lane, as the 128-byte-row layout
+// of the 128x128 kernel, which measures free of bank conflicts; the plain
+// (r >> 2) XOR of 64-byte rows measured two-way conflicts on gfx950.
+__device__ __forceinline__ int rho16(int r) { return 4 * ((r >> 1) & 3) + 2 * (r & 1) + ((r >> 3) & 1); }
+__device__ __forceinline__ int rho16_inv(int s) { return ((s & 1) << 3) | ((s >> 2) << 1) | ((s >> 1) & 1); }
+__device__ __forceinline__ int swz32(int r, int c) {
+  const int rl = r & 15;
+  return (r >> 4) * 1024 + rho16(rl) * 64 + ((c ^ ((rl >> 1) & 3)) << 4);
+}
+// byte offset of 16-byte chunk c of tile row r in a big-tile stage
+__device__ __forceinline__ int lswz(int r, int c) { return LBK == 32 ? swz32(r, c) : swz(r, c); }
 
 template <int KIND>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int mt, int ntiles) {
@@ -400,20 +423,28 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
   const int M = g.M, K = g.K;
   const int nk = (K + LBK - 1) / LBK;
 
-  // DMA plan: a wave instruction fills 16 rows x 64 B; wave w moves row
-  // groups w*2 + j (j = 0, 1) of A and of B (16 groups each per step).
+  // DMA plan: a wave instruction fills one 1 KB block (16 rows x 64 B or
+  // 8 rows x 128 B); wave w moves row groups w*kLGroups + j of A and of B.
   const uint32_t kOOB = 0x80000000u;
   __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
-  __amdgpu_buffer_rsrc_t rb[2];
-  uint32_t aoff[2], boff[2];
-  int lcol[2];
+  __amdgpu_buffer_rsrc_t rb[kLGroups];
+  uint32_t aoff[kLGroups], boff[kLGroups];
+  int lcol[kLGroups];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int grp = w * 2 + j;
-    const int row = grp * 16 + (lane >> 2);
-    lcol[j] = ((lane & 3) ^ ((row >> 2) & 3)) * 8;
+  for (int j = 0; j < kLGroups; ++j) {
+    const int grp = w * kLGroups + j;
+    int rl, ch;   // the row and the chunk whose slot this lane fills
+    if (LBK == 32) {
+      rl = rho16_inv(lane >> 2);
+      ch = (lane & 3) ^ ((rl >> 1) & 3);
+    } else {
+      rl = lane >> 3;
+      ch = (lane & 7) ^ (((grp * 8 + rl) >> 1) & 7);
+    }
+    const int row = grp * kLRows + rl;
+    lcol[j] = ch * 8;
     aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
-    const int r0 = grp * 16;
+    const int r0 = grp * kLRows;
     const void* base;
     int brow, nrows;
     if (g.B.mode == 0) {
@@ -427,22 +458,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
       nrows = g.B.n_feat;
     }
     rb[j] = make_rsrc(base, (uint32_t)((int64_t)(nrows > 0 ? nrows : 0) * K * 2));
-    const int myrow = brow + (lane >> 2);
+    const int myrow = brow + rl;
     boff[j] = myrow < nrows ? (uint32_t)((int64_t)myrow * K * 2) : kOOB;
   }
-  auto issue = [&](int stage, int k0) {
+  auto issue_group = [&](int stage, int k0, int j) {
     char* sa = smem + stage * kLStage;
     char* sb = sa + LBM * LBK * 2;
+    const int grp = w * kLGroups + j;
+    const int kk = k0 + lcol[j];
+    const bool kin = kk < K;
+    const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
+    const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+  };
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int grp = w * 2 + j;
-      const int kk = k0 + lcol[j];
-      const bool kin = kk < K;
-      const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
-      const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
-    }
+    for (int j = 0; j < kLGroups; ++j) issue_group(stage, k0, j);
   };
 
   f32x4_t acc[8][4];
@@ -452,19 +484,36 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int wm = (w >> 2) * 128, wn = (w & 3) * 64;
   const int fr = lane & 15, fc = lane >> 4;
-  auto compute = [&](int stage) {
+  // one step's MFMAs; with CB_BIG_ILV the next stage's DMA (when nstage >= 0)
+  // is issued a group at a time between them instead of in one burst
+  auto compute = [&](int stage, int nstage, int nk0) {
     const char* sa = smem + stage * kLStage;
     const char* sb = sa + LBM * LBK * 2;
-    bf16x8_t af[8], bfr[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
+    for (int ks = 0; ks < LBK / 32; ++ks) {
+      bf16x8_t af[8], bfr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + j * 16 + fr, fc));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + lswz(wm + i * 16 + fr, ks * 4 + fc));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + lswz(wn + j * 16 + fr, ks * 4 + fc));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+#if CB_BIG_ILV
+        constexpr int per = CB_BIG_ILV_PER > 0 ? CB_BIG_ILV_PER : 8 * (LBK / 32) / kLGroups;
+        const int slot = ks * 8 + i;
+        if (nstage >= 0 && slot % per == per - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_group(nstage, nk0, slot / per);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#endif
+      }
+    }
   };
 
 #pragma unroll
@@ -476,15 +525,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
       const int it = it0 + u;
       if (it < nk) {
         // this wave's step `it` landed once at most the later steps' loads
-        // (4 per step) are outstanding
+        // (2 kLGroups per step) are outstanding
         const int later = min(nk - 1 - it, LNS - 2);
-        if (later >= 3) CB_WAIT_VMCNT(12);
-        else if (later == 2) CB_WAIT_VMCNT(8);
-        else if (later == 1) CB_WAIT_VMCNT(4);
+        constexpr int PS = 2 * kLGroups;
+        if (later >= 3) CB_WAIT_VMCNT(3 * PS);
+        else if (later == 2) CB_WAIT_VMCNT(2 * PS);
+        else if (later == 1) CB_WAIT_VMCNT(PS);
         else CB_WAIT_VMCNT(0);
         CB_BARRIER();
-        if (it + LNS - 1 < nk) issue((u + LNS - 1) % LNS, (it + LNS - 1) * LBK);
-        compute(u);
+        const bool more = it + LNS - 1 < nk;
+#if CB_BIG_ILV
+        compute(u, more ? (u + LNS - 1) % LNS : -1, (it + LNS - 1) * LBK);
+#else
+        if (more) issue((u + LNS - 1) % LNS, (it + LNS - 1) * LBK);
+        compute(u, -1, 0);
+#endif
       }
     }
   }
