@@ -152,13 +152,17 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 #pragma unroll
       for (int r = 0; r < 4; ++r) *(u32x4_t*)(Ks + (kgk * 4 + r) * KLD + dck * 8) = rk[j][r];
       const int kg = u % (KT / 4), dc = u / (KT / 4);
-      // V^T: dims dc*8 .. +7, keys kg*4 .. +3 as one 8-byte store per dim
+      // V^T: dims dc*8 .. +7, keys kg*4 .. +3 as one 8-byte store per dim.
+      // Inside each 32-key block the key groups sit in the order 0 4 1 5 2 6
+      // 3 7, so that the 8 keys one lane feeds to an MFMA (4 from each half
+      // of the block) are one 16-byte read.
+      const int vcol = 32 * (kg >> 3) + 8 * (kg & 3) + 4 * ((kg >> 2) & 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int wsel = e >> 1, sh = (e & 1) * 16;
         const uint32_t v0 = (rv[j][0][wsel] >> sh) & 0xffffu, v1 = (rv[j][1][wsel] >> sh) & 0xffffu;
         const uint32_t v2 = (rv[j][2][wsel] >> sh) & 0xffffu, v3 = (rv[j][3][wsel] >> sh) & 0xffffu;
-        *(uint2*)(Vt + (dc * 8 + e) * VLD + kg * 4) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+        *(uint2*)(Vt + (dc * 8 + e) * VLD + vcol) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
       }
     }
     __syncthreads();
@@ -235,10 +239,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
     for (int mb = 0; mb < HD / 16; ++mb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16_t* vr = Vt + (mb * 16 + q) * VLD + st * 32 + 4 * gp;
-        const bf16x4_t lo = *reinterpret_cast<const bf16x4_t*>(vr);
-        const bf16x4_t hi = *reinterpret_cast<const bf16x4_t*>(vr + 16);
-        const bf16x8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(Vt + (mb * 16 + q) * VLD + st * 32 + 8 * gp);
         oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
         oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
       }
