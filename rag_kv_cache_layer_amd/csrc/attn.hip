@@ -38,7 +38,11 @@ namespace {
 
 constexpr int kRowTile = 32;     // query rows per workgroup (two 16-column MFMA blocks per wave)
 constexpr int kKeyTile = 64;     // keys per LDS stage
-constexpr int kKeySplit = 512;   // key-split boundary (multiple of kKeyTile)
+#ifndef CB_ATTN_SPLIT
+#define CB_ATTN_SPLIT 512
+#endif
+constexpr int kKeySplit = CB_ATTN_SPLIT;   // key-split boundary (multiple of kKeyTile)
+static_assert(kKeySplit % 64 == 0 && kKeySplit >= 512, "the partial buffers are sized for splits of >= 512 keys");
 
 template <int HD, int G>
 __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
