@@ -136,6 +136,25 @@ cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, int32_t r_las
  * cb_select_hkvd with n <= m_max candidates.  0 on invalid cfg. */
 size_t cb_workspace_size(const cb_layer_config* cfg, int32_t T, int32_t m_max);
 
+/* Bytes of device workspace needed by cb_blend_stack over T rows: the
+ * per-layer workspace of cb_workspace_size(cfg, T, T), two [T][d] hidden
+ * buffers and a [T] row list.  0 on invalid cfg or T <= 0. */
+size_t cb_stack_workspace_size(const cb_layer_config* cfg, int32_t T);
+
+/* Loading controller of section 5: the recompute ratio of one layer, in
+ * units of 1e-4.  The recompute delay of ratio r is modelled as r x
+ * t_prefill_us, the offline-profiled full prefill of one layer over the
+ * context (footnote 5); the load delay of one layer's KV as
+ * kv_bytes_per_token x n_tokens / link_bytes_per_us (footnote 6).  The ratio
+ * at which the two delays are equal, r_match = load / prefill, is rounded
+ * down to a multiple of 1e-4 (so the recompute stays within the load time)
+ * and capped at 1; the result is max(that, r_min_e4), the smallest ratio
+ * whose quality loss is negligible (the paper finds 15%, Figure 16).
+ * Returns -1 if a time, size or rate is not positive and finite, n_tokens
+ * <= 0, or r_min_e4 is outside [0, 10000]. */
+int32_t cb_pick_ratio(double t_prefill_us, double kv_bytes_per_token, int32_t n_tokens,
+                      double link_bytes_per_us, int32_t r_min_e4);
+
 const char* cb_status_string(cb_status s);
 
 /* hipError_t of the last failed HIP call on this thread (0 if none). */
@@ -229,6 +248,50 @@ cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_layer_weigh
                                 const cb_rope_dev* rope, const void* hidden_in, int32_t T,
                                 int32_t pos0, void* k_out, void* v_out, void* hidden_out,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* The fusor over a stack of n_layers layers (section 4.3, Figure 9), with
+ * each layer's KV loaded while the previous layer is recomputed (section 5,
+ * Figure 11: the fusor waits for the previous layer's recompute and for the
+ * layer's KV in GPU memory, then recomputes).
+ *  layers: host [n_layers] weight sets.  ks: host [n_layers] k_out per layer
+ *    (cb_filter_schedule).  Layer 0 recomputes every row from
+ *    first_chunk_len = chunk_offsets[1] (n_ctx when n_chunks = 1) to T-1;
+ *    layer l > 0 recomputes the rows layer l-1 kept.  Row counts: m_in_0 =
+ *    T - first_chunk_len; m_out_l = min(ks[l], m_in_l - q) + q with q =
+ *    T - n_ctx; m_in_{l+1} = m_out_l.  If m_rows_host is not NULL it
+ *    receives m_in_l, m_out_l for every layer (host [2*n_layers]).
+ *  k_caches, v_caches: device; layer l's cache [T][n_kv][hd] at element
+ *    offset l * layer_stride_elems.  On return (once the streams drain)
+ *    they hold the blended K/V of every layer.
+ *  k_src, v_src: both NULL, or both host [n_layers][T][n_kv][hd] (layer
+ *    stride T*n_kv*hd, allocate with hipHostMalloc for asynchronous copies)
+ *    holding each layer's chunk KV in context order.  When given, layer l's
+ *    K and V are copied into the device caches on copy_stream and layer l's
+ *    work on `stream` waits for those copies only; the copies of later
+ *    layers overlap the recompute.  copy_stream NULL = the copies run on
+ *    `stream`, in order, with no overlap.  The copies wait for work already
+ *    queued on `stream`.  When NULL, the device caches already hold the
+ *    chunk KV.
+ *  shift: nonzero = the chunk keys are at their local positions and are
+ *    re-aligned first (as cb_rope_shift; per layer after its copy when
+ *    loading, one launch over all layers otherwise); 0 = already aligned.
+ *  x_first: device [T - first_chunk_len][d], layer 0's input rows.
+ *  s_out_all: device int32 [sum_l m_out_l], layer l's kept rows at offset
+ *    sum_{j<l} m_out_j (ascending; layer l+1's input rows).
+ *  dev_all: device fp32 [sum_l m_in_l], layer l's deviations at offset
+ *    sum_{j<l} m_in_j (as dev_out of cb_blend_layer).
+ *  hidden_out: device [m_out_{n_layers-1}][d], the last layer's output for
+ *    its kept rows.
+ *  Workspace >= cb_stack_workspace_size(cfg, T).  The call creates and
+ *  releases one HIP event per layer (host objects; no device memory).
+ *  Errors as cb_blend_layer; nothing is enqueued when a check fails. */
+cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers, const cb_layer_weights* layers,
+                         const cb_rope_dev* rope, void* k_caches, void* v_caches,
+                         int64_t layer_stride_elems, const void* k_src, const void* v_src, int32_t T,
+                         const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
+                         const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all,
+                         void* hidden_out, int32_t* m_rows_host, void* ws, size_t ws_bytes,
+                         void* stream, void* copy_stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@
 // Every step is a kernel enqueued on the caller's stream; the host never
 // waits on the device.
 #include <math.h>
+
+#include <cmath>
 #include <string.h>
 
 #include <algorithm>
@@ -475,44 +477,32 @@ extern "C" cb_status cb_select_hkvd(const cb_layer_config* cfg, const void* k_ne
   return hip_status(launch_select(a, s));
 }
 
-extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
-                                    void* k_cache, void* v_cache, int32_t T, int32_t n_ctx, int32_t first_chunk_len,
-                                    const int32_t* s_in, int32_t m_in, const void* hidden_in,
-                                    const int32_t* in_rows, int32_t k_out, void* hidden_out, float* dev_out,
-                                    int32_t* s_out, int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
-  cb_status st = check_cfg(cfg);
-  if (st) return st;
-  st = check_weights(w);
-  if (st) return st;
-  if (!k_cache || !v_cache || !s_in || !hidden_in || !hidden_out || !s_out || !ws) return CB_ERR_ARG;
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(hidden_in) || !aligned16(hidden_out) ||
-      !aligned16(ws))
-    return CB_ERR_ARG;
-  if (T <= 0 || n_ctx < 0 || first_chunk_len < 0 || m_in < 0 || k_out < 0) return CB_ERR_ARG;
-  if (n_ctx > T || first_chunk_len > n_ctx) return CB_ERR_SHAPE;
+namespace cb {
+namespace {
+
+// One blend layer with validated arguments (shared by cb_blend_layer and
+// cb_blend_stack); m_in > 0.
+cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const cb_rope_dev& rope, void* k_cache,
+                    void* v_cache, int T, int n_ctx, int first_chunk_len, const int32_t* s_in, int m_in,
+                    const void* hidden_in, const int32_t* in_rows, int k_out, void* hidden_out, float* dev_out,
+                    int32_t* s_out, void* ws, hipStream_t s) {
+  const cb_layer_config* cfg = &c;
+  const cb_layer_weights* wp = &w;
   const int n_query = T - n_ctx;
   const int n_cand = m_in - n_query;
-  if (n_cand < 0 || n_cand > n_ctx - first_chunk_len) return CB_ERR_SHAPE;
-  if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
-  st = check_rope(rope, T);
-  if (st) return st;
-  if (ws_bytes < cb_workspace_size(cfg, T, m_in)) return CB_ERR_WORKSPACE;
   const int m_out = std::min(k_out, n_cand) + n_query;
-  if (m_out_host) *m_out_host = m_out;
-  if (m_in == 0) return CB_OK;
-
-  const Dims D(*cfg);
-  const Ws L = layout(*cfg, std::max(T, m_in), T);
-  hipStream_t s = (hipStream_t)stream;
-  const int dt = cfg->dtype;
+  const Dims D(c);
+  const Ws L = layout(c, std::max(T, m_in), T);
+  const int dt = c.dtype;
   const int n_src = in_rows ? T : m_in;
+  cb_status st;
 
   // 1. gather + attention RMSNorm
-  st = hip_status(launch_rmsnorm(dt, false, hidden_in, n_src, nullptr, in_rows, (const float*)w->attn_norm,
+  st = hip_status(launch_rmsnorm(dt, false, hidden_in, n_src, nullptr, in_rows, (const float*)wp->attn_norm,
                                  at<void>(ws, L.xn), m_in, D.d, cfg->rms_eps, s));
   if (st) return st;
   // 2. QKV + RoPE + deviation + K/V scatter
-  GemmArgs g = qkv_args(*cfg, *w, *rope, L, ws, m_in);
+  GemmArgs g = qkv_args(c, w, rope, L, ws, m_in);
   g.epi.rows = s_in;
   g.epi.pos0 = 0;
   g.epi.dev_lo = first_chunk_len;
@@ -556,7 +546,39 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
   // 5. O projection, MLP
-  return layer_tail(*cfg, *w, L, ws, m_out, hidden_in, n_src, at<int>(ws, L.sel), in_rows, hidden_out, s);
+  return layer_tail(c, w, L, ws, m_out, hidden_in, n_src, at<int>(ws, L.sel), in_rows, hidden_out, s);
+}
+
+}  // namespace
+}  // namespace cb
+
+extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
+                                    void* k_cache, void* v_cache, int32_t T, int32_t n_ctx, int32_t first_chunk_len,
+                                    const int32_t* s_in, int32_t m_in, const void* hidden_in,
+                                    const int32_t* in_rows, int32_t k_out, void* hidden_out, float* dev_out,
+                                    int32_t* s_out, int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  st = check_weights(w);
+  if (st) return st;
+  if (!k_cache || !v_cache || !s_in || !hidden_in || !hidden_out || !s_out || !ws) return CB_ERR_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(hidden_in) || !aligned16(hidden_out) ||
+      !aligned16(ws))
+    return CB_ERR_ARG;
+  if (T <= 0 || n_ctx < 0 || first_chunk_len < 0 || m_in < 0 || k_out < 0) return CB_ERR_ARG;
+  if (n_ctx > T || first_chunk_len > n_ctx) return CB_ERR_SHAPE;
+  const int n_query = T - n_ctx;
+  const int n_cand = m_in - n_query;
+  if (n_cand < 0 || n_cand > n_ctx - first_chunk_len) return CB_ERR_SHAPE;
+  if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
+  st = check_rope(rope, T);
+  if (st) return st;
+  if (ws_bytes < cb_workspace_size(cfg, T, m_in)) return CB_ERR_WORKSPACE;
+  const int m_out = std::min(k_out, n_cand) + n_query;
+  if (m_out_host) *m_out_host = m_out;
+  if (m_in == 0) return CB_OK;
+  return cb::blend_run(*cfg, *w, *rope, k_cache, v_cache, T, n_ctx, first_chunk_len, s_in, m_in, hidden_in, in_rows,
+                       k_out, hidden_out, dev_out, s_out, ws, (hipStream_t)stream);
 }
 
 extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_layer_weights* w,
@@ -608,4 +630,189 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
   return layer_tail(*cfg, *w, L, ws, T, hidden_in, T, nullptr, nullptr, hidden_out, s);
+}
+
+// ---------------------------------------------------------------------------
+// the fusor over a stack of layers, with KV loading pipelined with recompute
+// ---------------------------------------------------------------------------
+
+extern "C" size_t cb_stack_workspace_size(const cb_layer_config* cfg, int32_t T) {
+  if (check_cfg(cfg) != CB_OK || T <= 0) return 0;
+  const Dims D(*cfg);
+  return align256(cb_workspace_size(cfg, T, T)) + 2 * align256((size_t)T * D.d * D.b) + align256((size_t)T * 4);
+}
+
+extern "C" int32_t cb_pick_ratio(double t_prefill_us, double kv_bytes_per_token, int32_t n_tokens,
+                                 double link_bytes_per_us, int32_t r_min_e4) {
+  if (!(t_prefill_us > 0.0) || !(kv_bytes_per_token > 0.0) || !(link_bytes_per_us > 0.0) || n_tokens <= 0 ||
+      r_min_e4 < 0 || r_min_e4 > 10000 || !std::isfinite(t_prefill_us) || !std::isfinite(kv_bytes_per_token) ||
+      !std::isfinite(link_bytes_per_us))
+    return -1;
+  // T_load = bytes per token x tokens / link throughput; T_recompute(r) =
+  // r x T_prefill; equal at r_match = T_load / T_prefill
+  const double t_load = kv_bytes_per_token * (double)n_tokens / link_bytes_per_us;
+  const double r_match = t_load / t_prefill_us;
+  const double e4 = std::floor(r_match * 1e4);
+  const int32_t r = e4 >= 10000.0 ? 10000 : (int32_t)e4;
+  return std::max(r, r_min_e4);
+}
+
+extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers, const cb_layer_weights* layers,
+                                    const cb_rope_dev* rope, void* k_caches, void* v_caches,
+                                    int64_t layer_stride_elems, const void* k_src, const void* v_src, int32_t T,
+                                    const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
+                                    const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all,
+                                    void* hidden_out, int32_t* m_rows_host, void* ws, size_t ws_bytes, void* stream,
+                                    void* copy_stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (n_layers < 1 || !layers || !k_caches || !v_caches || !chunk_offsets || !x_first || !ks || !s_out_all ||
+      !dev_all || !hidden_out || !ws || T <= 0 || n_chunks < 1)
+    return CB_ERR_ARG;
+  if ((k_src == nullptr) != (v_src == nullptr)) return CB_ERR_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    st = check_weights(&layers[l]);
+    if (st) return st;
+    if (ks[l] < 0) return CB_ERR_ARG;
+  }
+  if (!aligned16(k_caches) || !aligned16(v_caches) || !aligned16(x_first) || !aligned16(hidden_out) ||
+      !aligned16(ws))
+    return CB_ERR_ARG;
+  if (n_chunks > 256) return CB_ERR_UNSUPPORTED;
+  if (chunk_offsets[0] != 0) return CB_ERR_SHAPE;
+  for (int c = 0; c < n_chunks; ++c)
+    if (chunk_offsets[c + 1] < chunk_offsets[c]) return CB_ERR_SHAPE;
+  const int n_ctx = chunk_offsets[n_chunks];
+  const int L0 = n_chunks > 1 ? chunk_offsets[1] : n_ctx;
+  if (n_ctx > T) return CB_ERR_SHAPE;
+  if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
+  const Dims D(*cfg);
+  const int64_t layer_elems = (int64_t)T * D.kv_dim;
+  if (n_layers > 1 && layer_stride_elems < layer_elems) return CB_ERR_SHAPE;
+  if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
+  st = check_rope(rope, T);
+  if (st) return st;
+  if (ws_bytes < cb_stack_workspace_size(cfg, T)) return CB_ERR_WORKSPACE;
+
+  // row counts of every layer, known on the host
+  const int n_query = T - n_ctx;
+  std::vector<int> m_in(n_layers), m_out(n_layers);
+  int rows = T - L0;
+  for (int l = 0; l < n_layers; ++l) {
+    m_in[l] = rows;
+    m_out[l] = std::min(ks[l], rows - n_query) + n_query;
+    rows = m_out[l];
+  }
+  if (m_rows_host)
+    for (int l = 0; l < n_layers; ++l) {
+      m_rows_host[2 * l] = m_in[l];
+      m_rows_host[2 * l + 1] = m_out[l];
+    }
+  if (m_in[0] == 0) return CB_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipStream_t cs = copy_stream ? (hipStream_t)copy_stream : s;
+  char* base = (char*)ws;
+  const size_t blend_bytes = align256(cb_workspace_size(cfg, T, T));
+  const size_t hid_bytes = align256((size_t)T * D.d * D.b);
+  void* hid[2] = {base + blend_bytes, base + blend_bytes + hid_bytes};
+  int* rows0 = (int*)(base + blend_bytes + 2 * hid_bytes);
+  st = hip_status(launch_iota(rows0, m_in[0], L0, s));
+  if (st) return st;
+
+  RopeShiftArgs ra{};
+  ra.layer_stride = layer_stride_elems;
+  ra.T = T;
+  ra.kv_dim = D.kv_dim;
+  ra.hd = D.hd;
+  ra.cos = rope->cos;
+  ra.sin = rope->sin;
+  ra.offsets = chunk_offsets;
+  ra.n_chunks = n_chunks;
+  const size_t layer_bytes = (size_t)layer_elems * D.b;
+  const int64_t stride_bytes = layer_stride_elems * D.b;
+
+  // KV loading (paper section 5): every layer's copies are queued on the copy
+  // stream up front; layer l waits only for its own copies, so the copies of
+  // later layers proceed while layer l is recomputed.
+  std::vector<hipEvent_t> ev;
+  auto cleanup = [&]() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  };
+  if (k_src) {
+    const bool pipelined = cs != s;
+    if (pipelined) {
+      // the copies must not start before earlier work on `stream` (which
+      // may still read the caches) has finished
+      hipEvent_t e0 = nullptr;
+      if ((st = hip_status(hipEventCreateWithFlags(&e0, hipEventDisableTiming)))) return st;
+      ev.push_back(e0);
+      if ((st = hip_status(hipEventRecord(e0, s))) || (st = hip_status(hipStreamWaitEvent(cs, e0, 0)))) {
+        cleanup();
+        return st;
+      }
+    }
+    for (int l = 0; l < n_layers; ++l) {
+      char* kd = (char*)k_caches + (int64_t)l * stride_bytes;
+      char* vd = (char*)v_caches + (int64_t)l * stride_bytes;
+      const char* kh = (const char*)k_src + (int64_t)l * layer_bytes;
+      const char* vh = (const char*)v_src + (int64_t)l * layer_bytes;
+      if ((st = hip_status(hipMemcpyAsync(kd, kh, layer_bytes, hipMemcpyHostToDevice, cs))) ||
+          (st = hip_status(hipMemcpyAsync(vd, vh, layer_bytes, hipMemcpyHostToDevice, cs)))) {
+        cleanup();
+        return st;
+      }
+      if (pipelined) {
+        hipEvent_t e = nullptr;
+        if ((st = hip_status(hipEventCreateWithFlags(&e, hipEventDisableTiming)))) {
+          cleanup();
+          return st;
+        }
+        ev.push_back(e);
+        if ((st = hip_status(hipEventRecord(e, cs)))) {
+          cleanup();
+          return st;
+        }
+      }
+    }
+  } else if (shift) {
+    // caches already on the device: one re-alignment launch for all layers
+    ra.k_cache = k_caches;
+    ra.n_layers = n_layers;
+    if ((st = hip_status(launch_rope_shift(cfg->dtype, ra, s)))) return st;
+  }
+
+  int64_t off_in = 0, off_out = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    void* kc = (char*)k_caches + (int64_t)l * stride_bytes;
+    void* vc = (char*)v_caches + (int64_t)l * stride_bytes;
+    if (k_src) {
+      if (ev.size() > 1 && (st = hip_status(hipStreamWaitEvent(s, ev[1 + l], 0)))) {
+        cleanup();
+        return st;
+      }
+      if (shift) {
+        ra.k_cache = kc;
+        ra.n_layers = 1;
+        if ((st = hip_status(launch_rope_shift(cfg->dtype, ra, s)))) {
+          cleanup();
+          return st;
+        }
+      }
+    }
+    if (m_in[l] == 0) continue;   // nothing left to recompute (no query rows, k = 0)
+    const int32_t* s_in = l == 0 ? rows0 : s_out_all + (off_out - m_out[l - 1]);
+    const void* x = l == 0 ? x_first : hid[(l - 1) & 1];
+    void* y = l == n_layers - 1 ? hidden_out : hid[l & 1];
+    st = blend_run(*cfg, layers[l], *rope, kc, vc, T, n_ctx, L0, s_in, m_in[l], x, nullptr, ks[l], y,
+                   dev_all + off_in, s_out_all + off_out, base, s);
+    if (st) {
+      cleanup();
+      return st;
+    }
+    off_in += m_in[l];
+    off_out += m_out[l];
+  }
+  cleanup();
+  return CB_OK;
 }

@@ -99,6 +99,9 @@ hipError_t launch_rope_shift(int dtype, const RopeShiftArgs& a, hipStream_t s);
 
 // RMSNorm of gathered rows: out[i] = x[map(i)] / sqrt(mean(x^2) + eps) * g.
 // x_f32 selects an fp32 input regardless of the storage dtype.
+// out[i] = start + i for i < n (the row list of a stack's first layer)
+hipError_t launch_iota(int* out, int n, int start, hipStream_t s);
+
 hipError_t launch_rmsnorm(int dtype, bool x_f32, const void* x, int n_src, const int* m1, const int* m2,
                           const float* g, void* out, int rows, int d, float eps, hipStream_t s);
 

@@ -693,10 +693,13 @@ int gemm_n_tiles(int dtype, const BOperand& B, int N) {
   return (N + bn - 1) / bn;
 }
 
+#ifndef CB_SPLIT_TILES
+#define CB_SPLIT_TILES 48
+#endif
 int gemm_splits(int dtype, int n_tiles, int K) {
   if (dtype != CB_BF16) return 1;
   int s = 1;
-  while (s < 4 && n_tiles * s < 64 && K / (2 * s) >= 1024) s *= 2;
+  while (s < 4 && n_tiles * s < CB_SPLIT_TILES && K / (2 * s) >= 1024) s *= 2;
   return s;
 }
 

@@ -64,4 +64,20 @@ hipError_t launch_rmsnorm(int dtype, bool x_f32, const void* x, int n_src, const
   return hipGetLastError();
 }
 
+namespace {
+
+__global__ __launch_bounds__(256) void iota_kernel(int* __restrict__ out, int n, int start) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = start + i;
+}
+
+}  // namespace
+
+hipError_t launch_iota(int* out, int n, int start, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  LaunchScope ls("iota", s);
+  iota_kernel<<<(n + 255) / 256, 256, 0, s>>>(out, n, start);
+  return hipGetLastError();
+}
+
 }  // namespace cb

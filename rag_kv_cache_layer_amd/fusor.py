@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         "cb_select_hkvd": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, SZ, P]),
         "cb_blend_layer": (I32, [CFG, W, R, P, P, I32, I32, I32, P, I32, P, P, I32, P, P, P, I32P, P, SZ, P]),
         "cb_full_prefill_layer": (I32, [CFG, W, R, P, I32, I32, P, P, P, P, SZ, P]),
+        "cb_stack_workspace_size": (SZ, [CFG, I32]),
+        "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
+        "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
+                                 P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -171,6 +175,20 @@ def filter_schedule(n_layers: int, r_first_e4: int, r_last_e4: int, n_ctx: int, 
 
 def workspace_size(cfg: LayerConfig, T: int, m_max: int) -> int:
     return int(lib().cb_workspace_size(ctypes.byref(cfg), T, m_max))
+
+
+def stack_workspace_size(cfg: LayerConfig, T: int) -> int:
+    return int(lib().cb_stack_workspace_size(ctypes.byref(cfg), T))
+
+
+def pick_ratio(t_prefill_us: float, kv_bytes_per_token: float, n_tokens: int, link_bytes_per_us: float,
+               r_min_e4: int = 1500) -> int:
+    """Loading controller's recompute ratio in units of 1e-4 (cb_pick_ratio)."""
+    r = int(lib().cb_pick_ratio(float(t_prefill_us), float(kv_bytes_per_token), int(n_tokens),
+                                float(link_bytes_per_us), int(r_min_e4)))
+    if r < 0:
+        raise CacheBlendError(1, "cb_pick_ratio")
+    return r
 
 
 def status_string(s: int) -> str:
@@ -336,4 +354,72 @@ def blend_stack(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: DeviceRop
                     s_out, ws, stream)
         out.append({"s_in": s, "dev": dv, "s_out": s_out, "y": y})
         s, x = s_out, y
+    return out
+
+
+def stack_rows(T: int, chunk_offsets: Sequence[int], ks: Sequence[int]):
+    """(m_in, m_out) per layer of cb_blend_stack, computed on the host."""
+    offs = [int(o) for o in chunk_offsets]
+    n_ctx = offs[-1]
+    L0 = offs[1] if len(offs) > 2 else n_ctx
+    q = T - n_ctx
+    rows, m_in, m_out = T - L0, [], []
+    for k in ks:
+        m_in.append(rows)
+        rows = min(int(k), rows - q) + q
+        m_out.append(rows)
+    return m_in, m_out
+
+
+def blend_stack_native(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: DeviceRope, k_caches, v_caches,
+                       T: int, chunk_offsets: Sequence[int], x_first, ks: Sequence[int], ws, k_src=None, v_src=None,
+                       shift: bool = True, stream=None, copy_stream=None):
+    """cb_blend_stack: the whole stack in one library call.
+
+    k_caches, v_caches: device [n_layers][T][n_kv][hd].  k_src, v_src: None,
+    or host tensors of the same shape (pinned for overlap) whose copies run on
+    copy_stream (a torch stream; None = on `stream`).  ws: uint8 device
+    tensor of stack_workspace_size bytes.  Returns a list of per-layer dicts
+    (dev, s_out as views into the concatenated outputs; y only for the last
+    layer), like blend_stack."""
+    torch = _torch()
+    n = len(layers)
+    dt = torch_dtype(cfg)
+    kv, d = cfg.n_kv_heads * cfg.head_dim, cfg.d_model
+    offs = np.ascontiguousarray(np.asarray(chunk_offsets, dtype=np.int32))
+    ks_a = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    if len(ks_a) != n:
+        raise ValueError("one k_out per layer")
+    m_in, m_out = stack_rows(T, offs, ks_a)
+    dev_ = x_first.device
+    s_all = torch.empty(max(sum(m_out), 1), dtype=torch.int32, device=dev_)
+    dev_all = torch.empty(max(sum(m_in), 1), dtype=torch.float32, device=dev_)
+    y = torch.empty((max(m_out[-1], 1), d), dtype=dt, device=dev_)
+    W = (LayerWeights * n)(*[l.struct for l in layers])
+    rows = (ctypes.c_int32 * (2 * n))()
+    if (k_src is None) != (v_src is None):
+        raise ValueError("k_src and v_src go together")
+    src = []
+    for name, t in (("k_src", k_src), ("v_src", v_src)):
+        if t is None:
+            src.append(None)
+            continue
+        if t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.numel() < n * T * kv:
+            raise ValueError(f"{name} must be a contiguous host tensor of {n * T * kv} {dt} elements")
+        src.append(ctypes.c_void_p(t.data_ptr()))
+    cs = None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
+    L0 = int(offs[1]) if len(offs) > 2 else int(offs[-1])
+    _check(lib().cb_blend_stack(ctypes.byref(cfg), n, W, ctypes.byref(rope.struct),
+                                _dptr(k_caches, "k_caches", dt, n * T * kv), _dptr(v_caches, "v_caches", dt, n * T * kv),
+                                T * kv, src[0], src[1], T, offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                len(offs) - 1, 1 if shift else 0, _dptr(x_first, "x_first", dt, (T - L0) * d),
+                                ks_a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _dptr(s_all, "s_out_all"),
+                                _dptr(dev_all, "dev_all"), _dptr(y, "hidden_out"), rows,
+                                _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), cs), "cb_blend_stack")
+    out, oi, oo = [], 0, 0
+    for l in range(n):
+        out.append({"dev": dev_all[oi:oi + m_in[l]], "s_out": s_all[oo:oo + m_out[l]]})
+        oi += m_in[l]
+        oo += m_out[l]
+    out[-1]["y"] = y[:m_out[-1]]
     return out
