@@ -249,6 +249,44 @@ cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_layer_weigh
                                 int32_t pos0, void* k_out, void* v_out, void* hidden_out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* One request of a batched fusor layer (cb_blend_batch): its own cache and
+ * geometry, as the arguments of the same name of cb_blend_layer. */
+typedef struct {
+  void* k_cache;             /* device [T][n_kv][hd], updated in place */
+  void* v_cache;
+  int32_t T;
+  int32_t n_ctx;
+  int32_t first_chunk_len;
+  int32_t m_in;              /* rows this request recomputes */
+  int32_t k_out;
+} cb_blend_request;
+
+/* One fusor layer for several requests at once: their recomputed rows are
+ * stacked into one set of projections (raising the row count of every GEMM),
+ * while the K deviation, the scatter, the top-k and the attention of each
+ * row use its own request's cache and geometry (section 4.2, Figure 5b, per
+ * request; section 7 measures throughput under many concurrent requests,
+ * Figure 14, and prefill time against batch size, Figure 15c).  For every request the result equals cb_blend_layer
+ * on that request alone, up to the rounding order of the attention key split
+ * (the split is chosen from the batch's row count).
+ *  reqs: host [n_req], 1 <= n_req <= 16.  m_out_r = min(k_out_r, m_in_r - q_r)
+ *    + q_r with q_r = T_r - n_ctx_r (host-computable).
+ *  s_in: device int32 [sum m_in]; request r's rows (ascending positions in
+ *    its own cache, every query row, none below first_chunk_len) at offset
+ *    sum_{j<r} m_in_j.  hidden_in: device [sum m_in][d], row i the input of
+ *    s_in[i].  hidden_out: device [sum m_out][d] and s_out: device int32
+ *    [sum m_out], request r's kept rows at offset sum_{j<r} m_out_j.
+ *    dev_out: device fp32 [sum m_in] or NULL.  m_out_host: host [n_req] or
+ *    NULL.
+ *  Workspace >= cb_workspace_size(cfg, max_r T_r, sum_r m_in_r); rope covers
+ *  max_r T_r positions.  CB_ERR_UNSUPPORTED for n_req > 16; other errors as
+ *  cb_blend_layer. */
+cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_weights* w,
+                         const cb_rope_dev* rope, int32_t n_req, const cb_blend_request* reqs,
+                         const int32_t* s_in, const void* hidden_in, void* hidden_out,
+                         float* dev_out, int32_t* s_out, int32_t* m_out_host, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* The fusor over a stack of n_layers layers (section 4.3, Figure 9), with
  * each layer's KV loaded while the previous layer is recomputed (section 5,
  * Figure 11: the fusor waits for the previous layer's recompute and for the

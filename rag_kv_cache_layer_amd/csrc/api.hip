@@ -816,3 +816,131 @@ extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers
   cleanup();
   return CB_OK;
 }
+
+// ---------------------------------------------------------------------------
+// several requests in one fusor layer
+// ---------------------------------------------------------------------------
+
+extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
+                                    int32_t n_req, const cb_blend_request* reqs, const int32_t* s_in,
+                                    const void* hidden_in, void* hidden_out, float* dev_out, int32_t* s_out,
+                                    int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  st = check_weights(w);
+  if (st) return st;
+  if (n_req < 1 || !reqs || !s_in || !hidden_in || !hidden_out || !s_out || !ws) return CB_ERR_ARG;
+  if (n_req > kMaxReq) return CB_ERR_UNSUPPORTED;
+  if (!aligned16(hidden_in) || !aligned16(hidden_out) || !aligned16(ws)) return CB_ERR_ARG;
+  int T_max = 1, M_in = 0, M_out = 0, tiles = 0;
+  std::vector<int> n_cand(n_req), m_out(n_req);
+  for (int r = 0; r < n_req; ++r) {
+    const cb_blend_request& q = reqs[r];
+    if (!q.k_cache || !q.v_cache || !aligned16(q.k_cache) || !aligned16(q.v_cache)) return CB_ERR_ARG;
+    if (q.T <= 0 || q.n_ctx < 0 || q.first_chunk_len < 0 || q.m_in < 0 || q.k_out < 0) return CB_ERR_ARG;
+    if (q.n_ctx > q.T || q.first_chunk_len > q.n_ctx) return CB_ERR_SHAPE;
+    n_cand[r] = q.m_in - (q.T - q.n_ctx);
+    if (n_cand[r] < 0 || n_cand[r] > q.n_ctx - q.first_chunk_len) return CB_ERR_SHAPE;
+    if (cfg->dtype == CB_F32 && q.T > kF32MaxT) return CB_ERR_UNSUPPORTED;
+    m_out[r] = std::min(q.k_out, n_cand[r]) + (q.T - q.n_ctx);
+    T_max = std::max(T_max, (int)q.T);
+    M_in += q.m_in;
+    M_out += m_out[r];
+    tiles += (m_out[r] + kAttnRowTile - 1) / kAttnRowTile;
+  }
+  st = check_rope(rope, T_max);
+  if (st) return st;
+  if (ws_bytes < cb_workspace_size(cfg, T_max, M_in)) return CB_ERR_WORKSPACE;
+  if (m_out_host)
+    for (int r = 0; r < n_req; ++r) m_out_host[r] = m_out[r];
+  if (M_in == 0) return CB_OK;
+
+  const cb_layer_config& c = *cfg;
+  const Dims D(c);
+  const Ws L = layout(c, std::max(T_max, M_in), T_max);
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = c.dtype;
+  // 1. attention RMSNorm of every request's rows
+  st = hip_status(launch_rmsnorm(dt, false, hidden_in, M_in, nullptr, nullptr, (const float*)w->attn_norm,
+                                 at<void>(ws, L.xn), M_in, D.d, c.rms_eps, s));
+  if (st) return st;
+  // 2. one QKV GEMM over all rows; each row's epilogue uses its own request's cache
+  GemmArgs g = qkv_args(c, *w, *rope, L, ws, M_in);
+  g.epi.rows = s_in;
+  g.epi.pos0 = 0;
+  g.epi.k_cache = reqs[0].k_cache;
+  g.epi.v_cache = reqs[0].v_cache;
+  g.epi.T = T_max;
+  g.epi.dev_part = at<float>(ws, L.devp);
+  ReqTable& rq = g.epi.req;
+  rq.n = n_req;
+  int off = 0;
+  for (int r = 0; r < n_req; ++r) {
+    rq.row_off[r] = off;
+    rq.k[r] = reqs[r].k_cache;
+    rq.v[r] = reqs[r].v_cache;
+    rq.T[r] = reqs[r].T;
+    rq.lo[r] = reqs[r].first_chunk_len;
+    rq.hi[r] = reqs[r].n_ctx;
+    off += reqs[r].m_in;
+  }
+  rq.row_off[n_req] = off;
+  st = hip_status(launch_gemm(dt, g, s));
+  if (st) return st;
+  // 3. one top-k per request
+  SelectArgs sa{};
+  sa.dev_part = at<float>(ws, L.devp);
+  sa.n_parts = D.n_k_tiles();
+  sa.ld_part = M_in;
+  sa.dev = dev_out ? dev_out : at<float>(ws, L.dev);
+  sa.n_cand = n_cand[0];
+  sa.m_in = reqs[0].m_in;
+  sa.k = reqs[0].k_out;
+  sa.ids_in = s_in;
+  sa.sel = at<int>(ws, L.sel);
+  sa.ids_out = s_out;
+  sa.n_seg = n_req;
+  int in_off = 0, out_off = 0;
+  for (int r = 0; r < n_req; ++r) {
+    sa.seg[r] = SelectArgs::Seg{in_off, reqs[r].m_in, n_cand[r], reqs[r].k_out, out_off};
+    in_off += reqs[r].m_in;
+    out_off += m_out[r];
+  }
+  st = hip_status(launch_select(sa, s));
+  if (st) return st;
+  // 4. attention: row tiles never straddle two requests
+  AttnArgs aa{};
+  aa.Q = at<void>(ws, L.q);
+  aa.qmap = at<int>(ws, L.sel);
+  aa.qpos = s_out;
+  aa.K = reqs[0].k_cache;
+  aa.V = reqs[0].v_cache;
+  aa.O = at<void>(ws, L.o);
+  aa.m = M_out;
+  aa.T = T_max;
+  aa.n_q = c.n_q_heads;
+  aa.n_kv = c.n_kv_heads;
+  aa.hd = D.hd;
+  aa.key_split = attn_key_split(dt, tiles * kAttnRowTile, c.n_q_heads, c.n_kv_heads);
+  aa.o_part = at<float>(ws, L.o_part);
+  aa.ml_part = at<float>(ws, L.ml_part);
+  aa.req.n = n_req;
+  int ro = 0, to = 0;
+  for (int r = 0; r < n_req; ++r) {
+    aa.req.row_off[r] = ro;
+    aa.req.tile_off[r] = to;
+    aa.req.k[r] = reqs[r].k_cache;
+    aa.req.v[r] = reqs[r].v_cache;
+    aa.req.T[r] = reqs[r].T;
+    ro += m_out[r];
+    to += (m_out[r] + kAttnRowTile - 1) / kAttnRowTile;
+  }
+  aa.req.row_off[n_req] = ro;
+  aa.req.tile_off[n_req] = to;
+  if (M_out > 0) {
+    st = hip_status(launch_attention(dt, aa, s));
+    if (st) return st;
+  }
+  // 5. O projection, MLP over all kept rows (residual rows via the selection)
+  return layer_tail(c, *w, L, ws, M_out, hidden_in, M_in, at<int>(ws, L.sel), nullptr, hidden_out, s);
+}

@@ -36,13 +36,39 @@ namespace cb {
 
 namespace {
 
-constexpr int kRowTile = 32;     // query rows per workgroup (two 16-column MFMA blocks per wave)
+constexpr int kRowTile = kAttnRowTile;   // query rows per workgroup
 constexpr int kKeyTile = 64;     // keys per LDS stage
 #ifndef CB_ATTN_SPLIT
 #define CB_ATTN_SPLIT 512
 #endif
 constexpr int kKeySplit = CB_ATTN_SPLIT;   // key-split boundary (multiple of kKeyTile)
 static_assert(kKeySplit % 64 == 0 && kKeySplit >= 512, "the partial buffers are sized for splits of >= 512 keys");
+
+// Rows, cache and length of a row tile.  With several requests each request's
+// rows start a new tile, so a tile never mixes caches.
+struct TileInfo {
+  int r0, r1, T;
+  const void* K;
+  const void* V;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const AttnArgs& a, int tile) {
+  if (a.req.n == 0) return TileInfo{tile * kRowTile, min(a.m, tile * kRowTile + kRowTile), a.T, a.K, a.V};
+  int r = 0;
+  while (r + 1 < a.req.n && a.req.tile_off[r + 1] <= tile) ++r;
+  const int r0 = a.req.row_off[r] + (tile - a.req.tile_off[r]) * kRowTile;
+  return TileInfo{r0, min(a.req.row_off[r + 1], r0 + kRowTile), a.req.T[r], a.req.k[r], a.req.v[r]};
+}
+
+__device__ __forceinline__ int tile_of_row(const AttnArgs& a, int i) {
+  if (a.req.n == 0) return i / kRowTile;
+  const int r = req_of_row(a.req, i);
+  return a.req.tile_off[r] + (i - a.req.row_off[r]) / kRowTile;
+}
+
+__host__ __device__ inline int n_row_tiles(const AttnArgs& a) {
+  return a.req.n == 0 ? (a.m + kRowTile - 1) / kRowTile : a.req.tile_off[a.req.n];
+}
 
 template <int HD, int G>
 __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
@@ -63,7 +89,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
   // so every row tile that reads one group's K/V shares an L2 and the XCDs
   // get equal mixes of key splits.  Latest row tiles (longest key ranges)
   // come first within a group.
-  const int n_tiles = (a.m + kRowTile - 1) / kRowTile;
+  const int n_tiles = n_row_tiles(a);
   const int n_groups = (int)gridDim.x / n_tiles;
   const int b = blockIdx.x;
   int grp, t;
@@ -78,6 +104,8 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
   const int tile = n_tiles - 1 - t;
   const int kvh = grp % a.n_kv;
   const int split = grp / a.n_kv;
+  const TileInfo ti = tile_info(a, tile);
+  const int T_rows = ti.T;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = kvh * G + w;
   const int q = lane & 15, gp = lane >> 4;
@@ -87,10 +115,10 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
   int pm = 0;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int i = tile * kRowTile + b * 16 + q;
-    valid[b] = i < a.m;
+    const int i = ti.r0 + b * 16 + q;
+    valid[b] = i < ti.r1;
     int p = valid[b] ? (a.qpos ? a.qpos[i] : i) : 0;
-    pos[b] = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+    pos[b] = p < 0 ? 0 : (p >= T_rows ? T_rows - 1 : p);
     pm = max(pm, pos[b]);
   }
 #pragma unroll
@@ -105,7 +133,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
   bf16x8_t qf[2][HD / 32];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int i = tile * kRowTile + b * 16 + q;
+    const int i = ti.r0 + b * 16 + q;
     const int qr = valid[b] ? (a.qmap ? a.qmap[i] : i) : 0;
     const gvec* Qp = (const gvec*)((const bf16_t*)a.Q + (int64_t)qr * ldq + head * HD + gp * 8);
 #pragma unroll
@@ -120,8 +148,8 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 #pragma unroll
     for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  const bf16_t* Kg = (const bf16_t*)a.K + kvh * HD;
-  const bf16_t* Vg = (const bf16_t*)a.V + kvh * HD;
+  const bf16_t* Kg = (const bf16_t*)ti.K + kvh * HD;
+  const bf16_t* Vg = (const bf16_t*)ti.V + kvh * HD;
 
   // staging: each thread moves 4 consecutive keys x 8 dims of K and of V.
   // For K the dim chunk varies fastest across lanes, so 16 lanes write one
@@ -137,10 +165,10 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
     const int kg = u % (KT / 4), dc = u / (KT / 4);                        \
     _Pragma("unroll") for (int r = 0; r < 4; ++r) {                        \
       int t = (T0) + kgk * 4 + r;                                          \
-      t = t < a.T ? t : a.T - 1; /* keys past T are masked below */       \
+      t = t < T_rows ? t : T_rows - 1; /* keys past T are masked below */ \
       rk[j][r] = *(const gvec*)(Kg + (int64_t)t * ldkv + dck * 8);         \
       int tv = (T0) + kg * 4 + r;                                          \
-      tv = tv < a.T ? tv : a.T - 1;                                        \
+      tv = tv < T_rows ? tv : T_rows - 1;                                  \
       rv[j][r] = *(const gvec*)(Vg + (int64_t)tv * ldkv + dc * 8);         \
     }                                                                      \
   }
@@ -254,7 +282,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     if (!valid[b]) continue;
-    const int i = tile * kRowTile + b * 16 + q;
+    const int i = ti.r0 + b * 16 + q;
     if (!splitting) {
       bf16_t* Op = (bf16_t*)a.O + (int64_t)i * ldq + head * HD + 4 * gp;
 #pragma unroll
@@ -291,13 +319,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __shared__ int s_pm;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  const int tile = i / kRowTile;   // workgroups of the attention kernel cover kRowTile rows
+  // the attention workgroup of this row's tile decided whether to split
+  const TileInfo ti = tile_info(a, tile_of_row(a, i));
   if (tid < 64) {
-    const int r = tile * kRowTile + tid;
+    const int r = ti.r0 + tid;
     int p = 0;
-    if (tid < kRowTile && r < a.m) {
+    if (tid < kRowTile && r < ti.r1) {
       p = a.qpos ? a.qpos[r] : r;
-      p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+      p = p < 0 ? 0 : (p >= ti.T ? ti.T - 1 : p);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o));
@@ -306,7 +335,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   __syncthreads();
   if (s_pm < a.key_split) return;   // this tile was written directly
   int p = a.qpos ? a.qpos[i] : i;
-  p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+  p = p < 0 ? 0 : (p >= ti.T ? ti.T - 1 : p);
   const int ns = p / a.key_split + 1;
   for (int head = tid; head < a.n_q; head += 256) {
     float m = -INFINITY;
@@ -345,15 +374,24 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, float scale) {
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int hd = a.hd;
   const int kvh = h / (a.n_q / a.n_kv);
+  const void* K = a.K;
+  const void* V = a.V;
+  int T_rows = a.T;
+  if (a.req.n > 0) {
+    const int r = req_of_row(a.req, i);
+    K = a.req.k[r];
+    V = a.req.v[r];
+    T_rows = a.req.T[r];
+  }
   int p = a.qpos ? a.qpos[i] : i;
-  p = p < 0 ? 0 : (p >= a.T ? a.T - 1 : p);
+  p = p < 0 ? 0 : (p >= T_rows ? T_rows - 1 : p);
   const int qr = a.qmap ? a.qmap[i] : i;
   const float* Qp = (const float*)a.Q + (int64_t)qr * a.n_q * hd + h * hd;
   for (int d = lane; d < hd; d += 64) qs[d] = Qp[d];
   __syncthreads();
   const int ldkv = a.n_kv * hd;
-  const float* Kg = (const float*)a.K + kvh * hd;
-  const float* Vg = (const float*)a.V + kvh * hd;
+  const float* Kg = (const float*)K + kvh * hd;
+  const float* Vg = (const float*)V + kvh * hd;
   float mx = -INFINITY;
   for (int t = lane; t <= p; t += 64) {
     const float* kr = Kg + (int64_t)t * ldkv;
@@ -386,7 +424,7 @@ template <int HD>
 hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
   const int g = a.n_q / a.n_kv;
   const int n_split = a.key_split > 0 ? (a.T + a.key_split - 1) / a.key_split : 1;
-  const dim3 grid((a.m + kRowTile - 1) / kRowTile * a.n_kv * n_split);
+  const dim3 grid(n_row_tiles(a) * a.n_kv * n_split);
   {
     LaunchScope ls("attention", s);
     switch (g) {

@@ -83,6 +83,29 @@ struct LaunchScope {
 // Launchers (host).  All return hipSuccess or the launch error.
 // ---------------------------------------------------------------------------
 
+// Several requests in one launch (the batched fusor): the rows of request r
+// are rows row_off[r] .. row_off[r+1]-1 of the launch, and each request has
+// its own K/V cache and length.  n = 0: one request, described by the
+// launch's scalar fields.  Read with a row (or tile) index in every kernel
+// that needs the cache of a row.
+constexpr int kMaxReq = 16;
+struct ReqTable {
+  int n;
+  int row_off[kMaxReq + 1];
+  int tile_off[kMaxReq + 1];   // attention: first row tile of request r
+  void* k[kMaxReq];
+  void* v[kMaxReq];
+  int T[kMaxReq];
+  int lo[kMaxReq], hi[kMaxReq];   // QKV: deviation for cache rows in [lo, hi)
+};
+
+// request of row `row` (rows of empty requests are skipped)
+__device__ __forceinline__ int req_of_row(const ReqTable& t, int row) {
+  int r = 0;
+  while (r + 1 < t.n && t.row_off[r + 1] <= row) ++r;
+  return r;
+}
+
 struct RopeShiftArgs {
   void* k_cache;
   int64_t layer_stride;
@@ -118,6 +141,13 @@ struct SelectArgs {
   int* sel;                // [m_out] kept entry positions, ascending (may be NULL)
   int* ids_out;            // [m_out] kept token ids (may be NULL)
   uint32_t* scratch;       // >= 16 words
+  // several requests: workgroup g selects within entries in_off .. in_off+m_in-1
+  // (the first n_cand are its candidates) and writes from out_off; sel values
+  // are positions in the whole entry list
+  int n_seg;               // 0 = one segment given by the fields above
+  struct Seg {
+    int in_off, m_in, n_cand, k, out_off;
+  } seg[kMaxReq];
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
@@ -158,6 +188,7 @@ struct EpiParams {
   int T;
   float* dev_part;        // [n_k_tiles][M] or NULL
   int k_tile0;            // first N tile intersecting the K columns
+  ReqTable req;           // several requests: caches, T and deviation rows per GEMM row range
   // RESID: out[i][c] = resid[map(i)][c] + acc
   const void* resid;
   int resid_f32;
@@ -185,6 +216,8 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Attention of selected rows over the cache.
 // ---------------------------------------------------------------------------
+constexpr int kAttnRowTile = 32;   // kept rows per attention workgroup (one row tile)
+
 struct AttnArgs {
   const void* Q;          // [*][n_q*hd]; row qmap[i] (NULL = i) holds query i
   const int* qmap;
@@ -196,6 +229,7 @@ struct AttnArgs {
   int key_split;          // 0: one pass over all keys; else keys split at multiples of this
   float* o_part;          // [T / key_split][m][n_q][hd] unnormalised partials (key_split > 0)
   float* ml_part;         // [T / key_split][m][n_q][2] running max (log2 units) and sum
+  ReqTable req;           // several requests: row ranges, row tiles, K/V and T per request (T = max)
 };
 // Key-split length used for m query rows (0 = none); chosen from the row and
 // head counts only.  attn_part_rows bounds the m for which it is non-zero.

@@ -78,7 +78,18 @@ __device__ __forceinline__ void rope8(float v[8], const float* cs, const float* 
 template <typename T>
 __device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8]) {
   const int crow = e.rows ? e.rows[gm] : gm;
-  if (crow < 0 || crow >= e.T) return 0.f;
+  void* k_cache = e.k_cache;
+  void* v_cache = e.v_cache;
+  int n_rows = e.T, dev_lo = e.dev_lo, dev_hi = e.dev_hi;
+  if (e.req.n > 0) {
+    const int r = req_of_row(e.req, gm);
+    k_cache = e.req.k[r];
+    v_cache = e.req.v[r];
+    n_rows = e.req.T[r];
+    dev_lo = e.req.lo[r];
+    dev_hi = e.req.hi[r];
+  }
+  if (crow < 0 || crow >= n_rows) return 0.f;
   const int pos = crow + e.pos0;
   if (c < e.q_dim + e.kv_dim) {
     const int dim = (c < e.q_dim ? c : c - e.q_dim) % e.hd;
@@ -90,12 +101,12 @@ __device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8]) {
     return 0.f;
   }
   if (c < e.q_dim + e.kv_dim) {
-    T* kp = (T*)e.k_cache + (int64_t)crow * e.kv_dim + (c - e.q_dim);
+    T* kp = (T*)k_cache + (int64_t)crow * e.kv_dim + (c - e.q_dim);
     float r[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) r[j] = Elem<T>::rnd(v[j]);
     float contrib = 0.f;
-    if (e.dev_part && crow >= e.dev_lo && crow < e.dev_hi) {
+    if (e.dev_part && crow >= dev_lo && crow < dev_hi) {
       float old[8];
       load8(kp, old);
 #pragma unroll
@@ -107,7 +118,7 @@ __device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8]) {
     store8(kp, r);
     return contrib;
   }
-  store8((T*)e.v_cache + (int64_t)crow * e.kv_dim + (c - e.q_dim - e.kv_dim), v);
+  store8((T*)v_cache + (int64_t)crow * e.kv_dim + (c - e.q_dim - e.kv_dim), v);
   return 0.f;
 }
 

@@ -64,33 +64,46 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ int s_total;
   __shared__ int s_bin, s_above;
   const int tid = threadIdx.x;
-  const int n = a.n_cand;
+  // this workgroup's segment (one per request when several are batched)
+  int in_off = 0, out_off = 0, n = a.n_cand, m_in = a.m_in, k_req = a.k;
+  if (a.n_seg > 0) {
+    const SelectArgs::Seg g = a.seg[blockIdx.x];
+    in_off = g.in_off;
+    out_off = g.out_off;
+    n = g.n_cand;
+    m_in = g.m_in;
+    k_req = g.k;
+  }
+  float* const dev = a.dev + in_off;
+  const int* const ids_in = a.ids_in ? a.ids_in + in_off : nullptr;
+  int* const sel = a.sel ? a.sel + out_off : nullptr;
+  int* const ids_out = a.ids_out ? a.ids_out + out_off : nullptr;
 
   // 1. deviation of every entry from the partial sums (fixed order)
   if (a.dev_part) {
-    for (int i = tid; i < a.m_in; i += kSelThreads) {
+    for (int i = tid; i < m_in; i += kSelThreads) {
       float s;
       if (i < n) {
         s = 0.f;
-        for (int t = 0; t < a.n_parts; ++t) s += a.dev_part[(int64_t)t * a.ld_part + i];
+        for (int t = 0; t < a.n_parts; ++t) s += a.dev_part[(int64_t)t * a.ld_part + in_off + i];
       } else {
         s = __builtin_nanf("");
       }
-      a.dev[i] = s;
+      dev[i] = s;
     }
     __syncthreads();
   }
 
-  const int n_query = a.m_in - n;
+  const int n_query = m_in - n;
   // 2. nothing to drop: keep every entry
-  if (a.k >= n) {
-    for (int i = tid; i < a.m_in; i += kSelThreads) {
-      if (a.sel) a.sel[i] = i;
-      if (a.ids_out) a.ids_out[i] = a.ids_in ? a.ids_in[i] : i;
+  if (k_req >= n) {
+    for (int i = tid; i < m_in; i += kSelThreads) {
+      if (sel) sel[i] = in_off + i;
+      if (ids_out) ids_out[i] = ids_in ? ids_in[i] : i;
     }
     return;
   }
-  const int k = a.k > 0 ? a.k : 0;
+  const int k = k_req > 0 ? k_req : 0;
 
   // 3. radix select of the k-th largest key
   uint32_t prefix = 0, hmask = 0;
@@ -100,7 +113,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += kSelThreads) {
-        const uint32_t key = order_key(a.dev[i]);
+        const uint32_t key = order_key(dev[i]);
         if ((key & hmask) == prefix) atomicAdd(&hist[(key >> sh) & 255u], 1);
       }
       __syncthreads();
@@ -147,12 +160,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const int lo = min(n, tid * seg), hi = min(n, lo + seg);
   int c_eq = 0;
   if (k > 0)
-    for (int i = lo; i < hi; ++i) c_eq += order_key(a.dev[i]) == tau;
+    for (int i = lo; i < hi; ++i) c_eq += order_key(dev[i]) == tau;
   int eq_seen = block_exclusive_scan(c_eq, wave_tot, &s_total);
   int c_keep = 0;
   if (k > 0)
     for (int i = lo; i < hi; ++i) {
-      const uint32_t key = order_key(a.dev[i]);
+      const uint32_t key = order_key(dev[i]);
       if (key > tau) ++c_keep;
       else if (key == tau) { if (eq_seen < take_eq) ++c_keep; ++eq_seen; }
     }
@@ -160,12 +173,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   if (k > 0) {
     eq_seen -= c_eq;  // back to this segment's base
     for (int i = lo; i < hi; ++i) {
-      const uint32_t key = order_key(a.dev[i]);
+      const uint32_t key = order_key(dev[i]);
       bool keep = key > tau;
       if (key == tau) { keep = eq_seen < take_eq; ++eq_seen; }
       if (keep) {
-        if (a.sel) a.sel[out] = i;
-        if (a.ids_out) a.ids_out[out] = a.ids_in ? a.ids_in[i] : i;
+        if (sel) sel[out] = in_off + i;
+        if (ids_out) ids_out[out] = ids_in ? ids_in[i] : i;
         ++out;
       }
     }
@@ -173,8 +186,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   // 5. query rows, always kept, after the candidates
   for (int j = tid; j < n_query; j += kSelThreads) {
     const int i = n + j;
-    if (a.sel) a.sel[k + j] = i;
-    if (a.ids_out) a.ids_out[k + j] = a.ids_in ? a.ids_in[i] : i;
+    if (sel) sel[k + j] = in_off + i;
+    if (ids_out) ids_out[k + j] = ids_in ? ids_in[i] : i;
   }
 }
 
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(256) void kdev_kernel(const T* __restrict__ k_new, 
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   LaunchScope ls("select_topk", s);
-  select_kernel<<<1, kSelThreads, 0, s>>>(a);
+  select_kernel<<<a.n_seg > 0 ? a.n_seg : 1, kSelThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -51,6 +51,12 @@ class RopeDev(ctypes.Structure):
     _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32)]
 
 
+class BlendRequest(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("T", ctypes.c_int32),
+                ("n_ctx", ctypes.c_int32), ("first_chunk_len", ctypes.c_int32), ("m_in", ctypes.c_int32),
+                ("k_out", ctypes.c_int32)]
+
+
 class KernelStat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double),
                 ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double)]
@@ -83,6 +89,7 @@ def lib() -> ctypes.CDLL:
         "cb_select_hkvd": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, SZ, P]),
         "cb_blend_layer": (I32, [CFG, W, R, P, P, I32, I32, I32, P, I32, P, P, I32, P, P, P, I32P, P, SZ, P]),
         "cb_full_prefill_layer": (I32, [CFG, W, R, P, I32, I32, P, P, P, P, SZ, P]),
+        "cb_blend_batch": (I32, [CFG, W, R, I32, ctypes.POINTER(BlendRequest), P, P, P, P, P, I32P, P, SZ, P]),
         "cb_stack_workspace_size": (SZ, [CFG, I32]),
         "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
         "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
@@ -297,6 +304,36 @@ def blend_layer(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, k_cache,
                                 _dptr(s_out, "s_out", torch.int32, m_exp), ctypes.byref(m_out),
                                 _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "cb_blend_layer")
     return int(m_out.value)
+
+
+def blend_batch(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, reqs: Sequence[dict], s_in, hidden_in,
+                hidden_out, dev_out, s_out, ws, stream=None):
+    """One fusor layer for several requests (cb_blend_batch).  reqs: dicts with
+    k_cache, v_cache (device tensors), T, n_ctx, first_chunk_len, m_in, k_out.
+    s_in / hidden_in / dev_out hold the requests' rows one after another;
+    hidden_out / s_out receive the kept rows likewise.  Returns m_out per
+    request."""
+    torch = _torch()
+    dt = torch_dtype(cfg)
+    kv, d = cfg.n_kv_heads * cfg.head_dim, cfg.d_model
+    n = len(reqs)
+    arr = (BlendRequest * n)()
+    m_in_tot = m_out_tot = 0
+    for i, r in enumerate(reqs):
+        arr[i] = BlendRequest(_dptr(r["k_cache"], "k_cache", dt, r["T"] * kv).value,
+                              _dptr(r["v_cache"], "v_cache", dt, r["T"] * kv).value, r["T"], r["n_ctx"],
+                              r["first_chunk_len"], r["m_in"], r["k_out"])
+        m_in_tot += r["m_in"]
+        m_out_tot += max(expected_m_out(r["T"], r["n_ctx"], r["m_in"], r["k_out"]), 0)
+    m_out = (ctypes.c_int32 * n)()
+    _check(lib().cb_blend_batch(ctypes.byref(cfg), ctypes.byref(layer.struct), ctypes.byref(rope.struct), n, arr,
+                                _dptr(s_in, "s_in", torch.int32, m_in_tot),
+                                _dptr(hidden_in, "hidden_in", dt, m_in_tot * d),
+                                _dptr(hidden_out, "hidden_out", dt, m_out_tot * d),
+                                _dptr(dev_out, "dev_out", torch.float32, m_in_tot),
+                                _dptr(s_out, "s_out", torch.int32, m_out_tot), m_out,
+                                _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "cb_blend_batch")
+    return [int(x) for x in m_out]
 
 
 def expected_m_out(T: int, n_ctx: int, m_in: int, k_out: int) -> int:

@@ -103,3 +103,27 @@ def test_stack_rejects_bad_arguments_before_any_device_work(cblib):
     assert call(n_layers=0) == 1
     assert call(stride=T * 256 - 8) == 2                      # layers overlap
     assert call(rope_=F.RopeDev(0x30000, 0x40000, T - 1)) == 2
+
+
+def test_batch_rejects_bad_arguments_before_any_device_work(cblib):
+    cfg = F.make_config(256, 4, 4, 64, 688, 1e4, 1e-5, "bf16")
+    w = F.LayerWeights(*[0x20000 + 256 * i for i in range(9)])
+    rope = F.RopeDev(0x30000, 0x40000, 200)
+
+    def req(T=144, n_ctx=128, L0=64, m_in=36, k=20, kc=0x50000):
+        return F.BlendRequest(kc, kc + 0x100000, T, n_ctx, L0, m_in, k)
+
+    def call(reqs, ws_bytes=1 << 40):
+        arr = (F.BlendRequest * max(len(reqs), 1))(*reqs)
+        return cblib.cb_blend_batch(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(rope), len(reqs), arr,
+                                    _fake(1), _fake(2), _fake(3), None, _fake(4), None, _fake(5), ws_bytes, None)
+
+    assert call([]) == 1                                  # no request
+    assert call([req()] * 17) == 5                        # more than 16 requests
+    assert call([req(), req(n_ctx=150)]) == 2             # n_ctx > T
+    assert call([req(), req(m_in=100)]) == 2              # more candidates than rows past the prefix
+    assert call([req(), req(m_in=10)]) == 2               # fewer rows than query rows
+    assert call([req(), req(kc=0x50008)]) == 1            # misaligned cache
+    assert call([req(), req(T=300, n_ctx=284, m_in=36)]) == 2   # rope table shorter than T
+    need = F.workspace_size(cfg, 144, 72)
+    assert call([req(), req()], need - 1) == 4
