@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra", action="store_true", help="also time the select call and full prefill")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="also time one batched fusor layer (cb_blend_batch) over this many copies of the request")
     ap.add_argument("--pipeline", action="store_true",
                     help="also measure the 32-layer stack with its KV loaded from pinned host memory "
                          "(loading alone, recompute alone, both pipelined)")
@@ -225,6 +227,50 @@ def main():
         torch.cuda.synchronize()
         extra["full_prefill_ms"] = round((time.perf_counter() - t0) * 100, 4)
 
+    if args.batch > 1:
+        # n_req requests of the same shape (own caches, same rows): one shift
+        # launch over all their caches + one batched layer
+        nb = args.batch
+        kvb = k_pre.unsqueeze(0).repeat(nb, 1, 1).contiguous()
+        vvb = v_pre.unsqueeze(0).repeat(nb, 1, 1).contiguous()
+        reqs = [dict(k_cache=kvb[i], v_cache=vvb[i], T=T, n_ctx=n_ctx, first_chunk_len=L0, m_in=m, k_out=k)
+                for i in range(nb)]
+        s_cat = S.repeat(nb).contiguous()
+        h_cat = h_full[S.long()].repeat(nb, 1).contiguous()
+        yb = torch.empty((nb * m, d), dtype=bf, device=dev)
+        dvb = torch.empty(nb * m, dtype=torch.float32, device=dev)
+        sob = torch.empty(nb * m, dtype=torch.int32, device=dev)
+        wsb = F.workspace(cfg, T, nb * m, dev)
+
+        def bstep():
+            F.rope_shift(cfg, rope, kvb, T * kvd, nb, T, offs)
+            F.blend_batch(cfg, layer, rope, reqs, s_cat, h_cat, yb, dvb, sob, wsb)
+
+        for _ in range(args.warmup):
+            bstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bstep()
+        torch.cuda.synchronize()
+        bms = (time.perf_counter() - t0) * 1e3 / args.steps
+        F.profile_begin()
+        for _ in range(args.steps):
+            bstep()
+        bstats = F.profile_end()
+        torch.cuda.synchronize()
+        bflops = {kname: v * nb for kname, v in flops.items()}
+        bk = {}
+        for name, st in bstats.items():
+            avg = st["total_ms"] / st["launches"]
+            e = {"avg_ms": round(avg, 5)}
+            if name in bflops:
+                e["frac_mfma"] = round(bflops[name] / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+            bk[name] = e
+        extra["batch"] = {"n_req": nb, "ms_per_step": round(bms, 5), "tokens_per_s": round(nb * T / (bms * 1e-3), 1),
+                          "speedup_vs_single_steps": round(nb * ms / bms, 3),
+                          "layer_frac_mfma": round(total_flops * nb / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "kernels": bk}
     if args.pipeline:
         extra["pipeline"] = pipeline_measure(seed)
 
