@@ -12,16 +12,21 @@
 // staged in LDS are shared by all heads that read them.  Each wave keeps its
 // 32 queries' Q fragments in registers (two 16-column MFMA blocks, so every
 // K or V fragment read from LDS feeds two MFMAs) and walks 64-key tiles with
-// an online softmax in fp32 (base-2 exponent); the next tile's loads are in
-// flight while the current one is computed.  Scores are formed transposed,
-// S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so every lane owns one query column:
-// the row statistics need only two cross-lane steps and the probabilities
-// feed the P V product (O^T += V^T P^T) straight from registers -- the K index
-// of an MFMA is a sum, so the same key permutation on both operands is exact.
-// V is stored transposed in LDS (8-byte stores of 4 keys) for that product.
-// A key tile past a query's position is an exact no-op for it (alpha = 1,
-// p = 0), so a row's result does not depend on the other rows of its tile.
-// Tiles holding the latest positions (the longest key ranges) go first.
+// an online softmax in fp32 (base-2 exponent).  K and V tiles reach LDS by
+// direct-to-LDS buffer loads into a ring of stages, the next tile's loads in
+// flight while the current one is computed; rows past T read as zero.
+// Scores are formed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), so
+// every lane owns one query column: the row statistics need only two
+// cross-lane steps and the probabilities feed the P V product (O^T += V^T
+// P^T) straight from registers -- the K index of an MFMA is a sum, so the
+// same key permutation on both operands is exact.  V stays in its natural
+// [key][dim] layout; its transposed operand comes from transposing LDS reads
+// (ds_read_b64_tr_b16).  Both tiles' 16-byte chunks are XOR-swizzled per row
+// so that these reads are free of bank conflicts.  The causal mask is applied
+// only on tiles that reach past some row's position.  A key tile past a
+// query's position is an exact no-op for it (alpha = 1, p = 0), so a row's
+// result does not depend on the other rows of its tile.  Tiles holding the
+// latest positions (the longest key ranges) go first.
 //
 // When there are too few (row tile, KV head) workgroups to fill the chip, the
 // keys are split at fixed multiples of 512: each split writes an unnormalised
@@ -30,6 +35,8 @@
 // result still does not either.
 //
 // fp32 path: one wave per (row, head); scores in LDS, two-pass softmax.
+#include <climits>
+
 #include "cb_internal.h"
 
 namespace cb {
@@ -38,11 +45,26 @@ namespace {
 
 constexpr int kRowTile = kAttnRowTile;   // query rows per workgroup
 constexpr int kKeyTile = 64;     // keys per LDS stage
+#ifndef CB_ATTN_NS
+#define CB_ATTN_NS 2
+#endif
+// K/V tiles in the LDS ring: 2 (64 KB at head_dim 128) leaves room for two
+// workgroups per CU, which measures faster than a deeper ring with one
+constexpr int kStages = CB_ATTN_NS;
+static_assert(kStages >= 2 && kStages <= 4, "ring depth");
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 #ifndef CB_ATTN_SPLIT
 #define CB_ATTN_SPLIT 512
 #endif
 constexpr int kKeySplit = CB_ATTN_SPLIT;   // key-split boundary (multiple of kKeyTile)
 static_assert(kKeySplit % 64 == 0 && kKeySplit >= 512, "the partial buffers are sized for splits of >= 512 keys");
+
+// One wave instruction: 16 bytes per lane from the buffer at byte offset
+// `off` into LDS at lds + 16 * lane (loads past the buffer's end write zero).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
 
 // Rows, cache and length of a row tile.  With several requests each request's
 // rows start a new tile, so a tile never mixes caches.
@@ -72,16 +94,22 @@ __host__ __device__ inline int n_row_tiles(const AttnArgs& a) {
 
 template <int HD, int G>
 __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
-  constexpr int NT = 64 * G;
   constexpr int KT = kKeyTile;
-  constexpr int KLD = HD + 8;                 // K tile row stride (bf16)
-  constexpr int VLD = KT + 8;                 // V^T tile row stride (bf16)
-  constexpr int UNITS = (KT / 4) * (HD / 8);  // 4 keys x 8 dims per unit
-  constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
-  constexpr bool PREFETCH = UPT <= 2;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VLD];
+  constexpr int ROWB = HD * 2;                // bytes of one key row of a head
+  constexpr int CPR = HD / 8;                 // 16-byte chunks per key row
+  constexpr int RPB = 1024 / ROWB;            // key rows per 1 KB block
+  constexpr int KPW = KT / RPB / G;           // blocks per tile that each wave loads
+  constexpr int kTile = KT * ROWB;            // bytes of a K (or V) tile
+  constexpr int kStage = 2 * kTile;
+  constexpr int NS = (G == 1 && kStages > 3) ? 3 : kStages;   // DMA wait counts stay below 64
+  static_assert(KPW >= 1 && KPW * RPB * G == KT, "tile rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   typedef __attribute__((address_space(1))) const u32x4_t gvec;
+  // slot of 16-byte chunk c in key row r is c ^ fk(r) (K) or c ^ fv(r) (V):
+  // K's fragment reads (16 rows, one chunk) and V's transposing reads (4
+  // rows x 2 chunks per 16 lanes) then spread over all banks
+  auto fk = [](int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto fv = [](int r) { return HD == 128 ? ((r & 3) << 1) | (((r >> 2) & 1) << 3) : ((r & 3) << 1); };
 
   // 1-D grid over (group = KV head + n_kv * key split, row tile).  Workgroups
   // are dealt round-robin to the 8 XCDs, each with its own L2; when the group
@@ -112,7 +140,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 
   int pos[2];
   bool valid[2];
-  int pm = 0;
+  int pm = 0, pmin = INT_MAX;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int i = ti.r0 + b * 16 + q;
@@ -120,9 +148,13 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
     int p = valid[b] ? (a.qpos ? a.qpos[i] : i) : 0;
     pos[b] = p < 0 ? 0 : (p >= T_rows ? T_rows - 1 : p);
     pm = max(pm, pos[b]);
+    if (valid[b]) pmin = min(pmin, pos[b]);
   }
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) pm = max(pm, __shfl_xor(pm, o));
+  for (int o = 1; o < 16; o <<= 1) {
+    pm = max(pm, __shfl_xor(pm, o));
+    pmin = min(pmin, __shfl_xor(pmin, o));
+  }
   // key range of this workgroup
   const bool splitting = a.key_split > 0 && pm >= a.key_split;
   const int k_lo = a.key_split > 0 ? split * a.key_split : 0;
@@ -148,136 +180,162 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 #pragma unroll
     for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  const bf16_t* Kg = (const bf16_t*)ti.K + kvh * HD;
-  const bf16_t* Vg = (const bf16_t*)ti.V + kvh * HD;
+  // K/V of this KV head through buffer resources: rows at or past T lie
+  // past the resource's end and load as zero (they are masked), and a
+  // tile's row offset is a scalar operand
+  const uint32_t row_bytes = (uint32_t)ldkv * 2;
+  const uint32_t kv_span = (uint32_t)((int64_t)T_rows * ldkv * 2 - (int64_t)kvh * HD * 2);
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc((const bf16_t*)ti.K + kvh * HD, kv_span);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc((const bf16_t*)ti.V + kvh * HD, kv_span);
 
-  // staging: each thread moves 4 consecutive keys x 8 dims of K and of V.
-  // For K the dim chunk varies fastest across lanes, so 16 lanes write one
-  // key row contiguously (conflict-free LDS stores); for V the key group
-  // varies fastest, which suits its transposed 8-byte stores.  Threads past
-  // the last unit load a valid duplicate and never store it, so the loads
-  // carry no branch.
-  u32x4_t rk[UPT][4], rv[UPT][4];
-#define CB_ATTN_FETCH(T0)                                                  \
-  _Pragma("unroll") for (int j = 0; j < UPT; ++j) {                        \
-    const int u = min(tid + j * NT, UNITS - 1);                            \
-    const int kgk = u / (HD / 8), dck = u % (HD / 8);                      \
-    const int kg = u % (KT / 4), dc = u / (KT / 4);                        \
-    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                        \
-      int t = (T0) + kgk * 4 + r;                                          \
-      t = t < T_rows ? t : T_rows - 1; /* keys past T are masked below */ \
-      rk[j][r] = *(const gvec*)(Kg + (int64_t)t * ldkv + dck * 8);         \
-      int tv = (T0) + kg * 4 + r;                                          \
-      tv = tv < T_rows ? tv : T_rows - 1;                                  \
-      rv[j][r] = *(const gvec*)(Vg + (int64_t)tv * ldkv + dc * 8);         \
-    }                                                                      \
+  // LDS ring of NS stages, each a K tile and a V tile of KT keys in their
+  // natural [key][dim] layout, filled by direct-to-LDS loads: one wave
+  // instruction fills a 1 KB block of RPB key rows; lane L fills 16-byte slot
+  // L % CPR of row L / CPR with the dim chunk slot ^ f(row).
+  const int n_it = (k_hi - k_lo + KT - 1) / KT;
+  uint32_t kof[KPW], vof[KPW];
+#pragma unroll
+  for (int j = 0; j < KPW; ++j) {
+    const int blk = w * KPW + j;   // 1 KB block of the tile
+    const int row = blk * RPB + lane / CPR;
+    const int slot = lane % CPR;
+    kof[j] = (uint32_t)row * row_bytes + (uint32_t)((slot ^ fk(row)) << 4);
+    vof[j] = (uint32_t)row * row_bytes + (uint32_t)((slot ^ fv(row)) << 4);
   }
+  auto issue = [&](int stage, int t0) {
+    char* sk = smem + stage * kStage;
+    char* sv = sk + kTile;
+    const uint32_t so = (uint32_t)t0 * row_bytes;
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int blk = w * KPW + j;
+      dma16(rK, sk + blk * 1024, kof[j] + so);
+      dma16(rV, sv + blk * 1024, vof[j] + so);
+    }
+  };
+  // V^T operand reads: lane L = 16 g + 4 j + c4 points at the 4 dims
+  // 16 mb + 4 c4 .. +3 of key 32 st + 4 g + j (+ 16 for the second read);
+  // the transposing read hands lane 16 g + i the values of dim 16 mb + i for
+  // the 4 keys, i.e. k slots 8 g .. 8 g + 7 of the MFMA's A operand
+  const int tj = (lane >> 2) & 3, tc = lane & 3;
+  const int tkey = 4 * gp + tj;                           // + 32 st (+ 16)
 
-  if (PREFETCH) { CB_ATTN_FETCH(k_lo) }
-  for (int t0 = k_lo; t0 < k_hi; t0 += KT) {
-    if (!PREFETCH) { CB_ATTN_FETCH(t0) }
 #pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = tid + j * NT;
-      if (UNITS % NT != 0 && u >= UNITS) continue;
-      const int kgk = u / (HD / 8), dck = u % (HD / 8);
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < n_it) issue(st, k_lo + st * KT);
+  for (int it0 = 0; it0 < n_it; it0 += NS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *(u32x4_t*)(Ks + (kgk * 4 + r) * KLD + dck * 8) = rk[j][r];
-      const int kg = u % (KT / 4), dc = u / (KT / 4);
-      // V^T: dims dc*8 .. +7, keys kg*4 .. +3 as one 8-byte store per dim.
-      // Inside each 32-key block the key groups sit in the order 0 4 1 5 2 6
-      // 3 7, so that the 8 keys one lane feeds to an MFMA (4 from each half
-      // of the block) are one 16-byte read.
-      const int vcol = 32 * (kg >> 3) + 8 * (kg & 3) + 4 * ((kg >> 2) & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wsel = e >> 1, sh = (e & 1) * 16;
-        const uint32_t v0 = (rv[j][0][wsel] >> sh) & 0xffffu, v1 = (rv[j][1][wsel] >> sh) & 0xffffu;
-        const uint32_t v2 = (rv[j][2][wsel] >> sh) & 0xffffu, v3 = (rv[j][3][wsel] >> sh) & 0xffffu;
-        *(uint2*)(Vt + (dc * 8 + e) * VLD + vcol) = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-      }
-    }
-    __syncthreads();
-    if (PREFETCH && t0 + KT < k_hi) { CB_ATTN_FETCH(t0 + KT) }   // next tile's loads overlap this tile's math
+    for (int u = 0; u < NS; ++u) {
+      const int it = it0 + u;
+      if (it >= n_it) break;
+      const int t0 = k_lo + it * KT;
+      // this wave's loads of tile `it` landed once at most the later tiles'
+      // loads are outstanding; then every wave's have (barrier)
+      const int later = min(n_it - 1 - it, NS - 2);
+      if (later >= 2) CB_WAIT_VMCNT(4 * KPW);
+      else if (later == 1) CB_WAIT_VMCNT(2 * KPW);
+      else CB_WAIT_VMCNT(0);
+      CB_BARRIER();
+      if (it + NS - 1 < n_it) issue((u + NS - 1) % NS, t0 + (NS - 1) * KT);
+      const char* sk = smem + u * kStage;
+      const char* sv = sk + kTile;
 
-    // S^T[key][query]: lane holds keys t0+16kb+4gp+v of queries q (b=0) and 16+q (b=1)
-    f32x4_t s[2][4];
+      // S^T[key][query]: lane holds keys t0+16kb+4gp+v of queries q (b=0) and 16+q (b=1)
+      f32x4_t s[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) {
+        s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int key = kb * 16 + q;
 #pragma unroll
-      for (int ks = 0; ks < HD / 32; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 16 + q) * KLD + ks * 32 + gp * 8);
-        s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
-        s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
+        for (int ks = 0; ks < HD / 32; ++ks) {
+          const int c = ks * 4 + gp;
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(sk + key * ROWB + ((c ^ fk(key)) << 4));
+          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
+        }
       }
-    }
-    // online softmax per query, in base-2 units (x = s * scale_log2, one
-    // fused multiply-add inside the exponent); the output accumulators are
-    // rescaled only when some query's running max grew -- otherwise alpha is
-    // exactly 1 for every lane and the multiply is skipped
-    bf16x8_t pb[2][2];
-    bool grew = false;
-    float alpha[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = t0 + kb * 16 + 4 * gp + v;
-          const float x = key <= pos[b] ? s[b][kb][v] : -INFINITY;
-          s[b][kb][v] = x;
-          mx = fmaxf(mx, x);
+      // online softmax per query, in base-2 units (x = s * scale_log2, one
+      // fused multiply-add inside the exponent); the output accumulators are
+      // rescaled only when some query's running max grew -- otherwise alpha is
+      // exactly 1 for every lane and the multiply is skipped
+      bf16x8_t pb[2][2];
+      bool grew = false;
+      float alpha[2];
+      // causal mask only on tiles that reach past some row's position
+      // (uniform: every wave of the workgroup has the same rows)
+      const bool masked = t0 + KT - 1 > pmin;
+  #pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float mx = -INFINITY;
+        if (masked) {
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int key = t0 + kb * 16 + 4 * gp + v;
+              const float x = key <= pos[b] ? s[b][kb][v] : -INFINITY;
+              s[b][kb][v] = x;
+              mx = fmaxf(mx, x);
+            }
+        } else {
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[b][kb][v]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[b], mx * scale_log2);
-      grew |= m_new > m_run[b];
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
-      alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use);
-      float sum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][kb][v], scale_log2, -m_use));
-          s[b][kb][v] = e;
-          sum += e;
-        }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      l_run[b] = l_run[b] * alpha[b] + sum;
-      m_run[b] = m_new;
-      // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j
-      // (j<4) or 32st+16+4gp+(j-4), matching the V^T reads below
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          pb[b][st][v] = (__bf16)s[b][2 * st][v];
-          pb[b][st][4 + v] = (__bf16)s[b][2 * st + 1][v];
-        }
-    }
-    if (__any(grew)) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha[b];
-    }
-#pragma unroll
-    for (int mb = 0; mb < HD / 16; ++mb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(Vt + (mb * 16 + q) * VLD + st * 32 + 8 * gp);
-        oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
-        oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[b], mx * scale_log2);
+        grew |= m_new > m_run[b];
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
+        alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use);
+        float sum = 0.f;
+  #pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][kb][v], scale_log2, -m_use));
+            s[b][kb][v] = e;
+            sum += e;
+          }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        l_run[b] = l_run[b] * alpha[b] + sum;
+        m_run[b] = m_new;
+        // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j
+        // (j<4) or 32st+16+4gp+(j-4), matching the V^T reads below
+  #pragma unroll
+        for (int st = 0; st < 2; ++st)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            pb[b][st][v] = (__bf16)s[b][2 * st][v];
+            pb[b][st][4 + v] = (__bf16)s[b][2 * st + 1][v];
+          }
       }
-    __syncthreads();
+      if (__any(grew)) {
+  #pragma unroll
+        for (int b = 0; b < 2; ++b)
+  #pragma unroll
+          for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha[b];
+      }
+  #pragma unroll
+      for (int mb = 0; mb < HD / 16; ++mb)
+  #pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int c = 2 * mb + (tc >> 1), h8 = (tc & 1) * 8;
+          const int k1 = 32 * st + tkey, k2 = k1 + 16;
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(sv + k1 * ROWB + ((c ^ fv(k1)) << 4) + h8));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(sv + k2 * ROWB + ((c ^ fv(k2)) << 4) + h8));
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
+          oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
+        }
+    }
   }
-#undef CB_ATTN_FETCH
+  CB_WAIT_VMCNT(0);
 
 #pragma unroll
   for (int b = 0; b < 2; ++b) {

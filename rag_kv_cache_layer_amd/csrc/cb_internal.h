@@ -99,6 +99,26 @@ struct ReqTable {
   int lo[kMaxReq], hi[kMaxReq];   // QKV: deviation for cache rows in [lo, hi)
 };
 
+// s_waitcnt vmcnt(n) lgkmcnt(0): this wave's LDS DMA up to the n most recent
+// loads has landed and its LDS reads have returned.
+#define CB_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
+// Workgroup barrier without a memory fence (a fence would drain the DMA ring);
+// the empty asm statements keep the compiler from moving LDS accesses across it.
+#define CB_BARRIER()                  \
+  do {                                \
+    asm volatile("" ::: "memory");    \
+    __builtin_amdgcn_s_barrier();     \
+    asm volatile("" ::: "memory");    \
+  } while (0)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at p (gfx9 layout: raw buffer, no
+// stride); loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // request of row `row` (rows of empty requests are skipped)
 __device__ __forceinline__ int req_of_row(const ReqTable& t, int row) {
   int r = 0;

@@ -207,24 +207,7 @@ __device__ __forceinline__ int xcd_remap(int id, int nb) {
   return (nb & 7) == 0 ? (id & 7) * (nb >> 3) + (id >> 3) : id;
 }
 
-// s_waitcnt vmcnt(n) lgkmcnt(0): this wave's LDS DMA up to the n most recent
-// loads has landed and its LDS reads have returned.
-#define CB_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
-// Workgroup barrier without a memory fence (a fence would drain the DMA ring);
-// the empty asm statements keep the compiler from moving LDS accesses across it.
-#define CB_BARRIER()                  \
-  do {                                \
-    asm volatile("" ::: "memory");    \
-    __builtin_amdgcn_s_barrier();     \
-    asm volatile("" ::: "memory");    \
-  } while (0)
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Buffer resource over `bytes` bytes at p (gfx9 layout: raw buffer, no stride).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 
 // Byte offset of 16-byte chunk c of row r in a swizzled [rows][BK] bf16 tile:
 // rows are 128 B, chunk c of row r sits in slot c ^ ((r >> 1) & 7), so the
@@ -236,6 +219,9 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >>
 #endif
 #ifndef CB_GEMM_MINBLOCKS
 #define CB_GEMM_MINBLOCKS 1
+#endif
+#ifndef CB_GEMM_ILV
+#define CB_GEMM_ILV 1
 #endif
 constexpr int NSTAGE = CB_GEMM_NSTAGE;          // LDS ring depth (K steps in flight)
 constexpr int kStageBytes = (BM + BN) * BK * 2;  // 32 KB
@@ -290,19 +276,20 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     boff[j] = myrow < nrows ? (uint32_t)((int64_t)myrow * K * 2) : kOOB;
   }
 
-  auto issue = [&](int stage, int k0) {
+  auto issue_group = [&](int stage, int k0, int j) {
     char* sa = smem + stage * kStageBytes;
     char* sb = sa + BM * BK * 2;
+    const int grp = w * 4 + j;
+    const int kk = k0 + lcol[j];
+    const bool kin = kk < ke;
+    const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
+    const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+  };
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int grp = w * 4 + j;
-      const int kk = k0 + lcol[j];
-      const bool kin = kk < ke;
-      const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
-      const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) issue_group(stage, k0, j);
   };
 
   f32x4_t acc[4][4];
@@ -313,7 +300,9 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   const int fr = lane & 15, fc = lane >> 4;
 
-  auto compute = [&](int stage) {
+  // one step's MFMAs; with CB_GEMM_ILV the next stage's DMA (nstage >= 0) is
+  // issued one row group at a time between them
+  auto compute = [&](int stage, int nstage, int nk0) {
     const char* sa = smem + stage * kStageBytes;
     const char* sb = sa + BM * BK * 2;
 #pragma unroll
@@ -325,10 +314,19 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
         bfr[i] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn + i * 16 + fr, ks * 4 + fc));
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+#if CB_GEMM_ILV
+        const int slot = ks * 4 + i;   // 8 slots per step, 4 row groups to issue
+        if (nstage >= 0 && (slot & 1)) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue_group(nstage, nk0, slot >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#endif
+      }
     }
   };
 
@@ -347,8 +345,13 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
         if (it + 1 < nk) CB_WAIT_VMCNT(8 * (NSTAGE - 2));
         else CB_WAIT_VMCNT(0);
         CB_BARRIER();   // every wave's step `it` is in LDS; step it-1's buffer is free
-        if (it + NSTAGE - 1 < nk) issue((u + NSTAGE - 1) % NSTAGE, kb + (it + NSTAGE - 1) * BK);
-        compute(u);
+        const bool more = it + NSTAGE - 1 < nk;
+#if CB_GEMM_ILV
+        compute(u, more ? (u + NSTAGE - 1) % NSTAGE : -1, kb + (it + NSTAGE - 1) * BK);
+#else
+        if (more) issue((u + NSTAGE - 1) % NSTAGE, kb + (it + NSTAGE - 1) * BK);
+        compute(u, -1, 0);
+#endif
       }
     }
   }
