@@ -44,9 +44,16 @@ namespace cb {
 namespace {
 
 constexpr int kRowTile = kAttnRowTile;   // query rows per workgroup
-constexpr int kKeyTile = 64;     // keys per LDS stage
+#ifndef CB_ATTN_KT
+#define CB_ATTN_KT 64
+#endif
+constexpr int kKeyTile = CB_ATTN_KT;   // keys per LDS stage (32 or 64)
+static_assert(kKeyTile == 32 || kKeyTile == 64, "key tile");
 #ifndef CB_ATTN_NS
 #define CB_ATTN_NS 2
+#endif
+#ifndef CB_ATTN_MINB
+#define CB_ATTN_MINB 2
 #endif
 // K/V tiles in the LDS ring: 2 (64 KB at head_dim 128) leaves room for two
 // workgroups per CU, which measures faster than a deeper ring with one
@@ -93,8 +100,10 @@ __host__ __device__ inline int n_row_tiles(const AttnArgs& a) {
 }
 
 template <int HD, int G>
-__global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
-  constexpr int KT = kKeyTile;
+__global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_kernel(AttnArgs a, float scale_log2) {
+  constexpr int KT = HD == 128 ? kKeyTile : 64;   // a head_dim-64 tile of 32 keys is too small for 8 waves
+  constexpr int KB = KT / 16;                      // 16-key score blocks per tile
+  constexpr int KS = KT / 32;                      // 32-key PV steps per tile
   constexpr int ROWB = HD * 2;                // bytes of one key row of a head
   constexpr int CPR = HD / 8;                 // 16-byte chunks per key row
   constexpr int RPB = 1024 / ROWB;            // key rows per 1 KB block
@@ -241,9 +250,9 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
       const char* sv = sk + kTile;
 
       // S^T[key][query]: lane holds keys t0+16kb+4gp+v of queries q (b=0) and 16+q (b=1)
-      f32x4_t s[2][4];
+      f32x4_t s[2][KB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         const int key = kb * 16 + q;
@@ -259,19 +268,19 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
       // fused multiply-add inside the exponent); the output accumulators are
       // rescaled only when some query's running max grew -- otherwise alpha is
       // exactly 1 for every lane and the multiply is skipped
-      bf16x8_t pb[2][2];
+      bf16x8_t pb[2][KS];
       bool grew = false;
       float alpha[2];
       // causal mask only on tiles that reach past some row's position
       // (uniform: every wave of the workgroup has the same rows)
       const bool masked = t0 + KT - 1 > pmin;
-  #pragma unroll
+#pragma unroll
       for (int b = 0; b < 2; ++b) {
         float mx = -INFINITY;
         if (masked) {
-  #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int key = t0 + kb * 16 + 4 * gp + v;
               const float x = key <= pos[b] ? s[b][kb][v] : -INFINITY;
@@ -279,9 +288,9 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
               mx = fmaxf(mx, x);
             }
         } else {
-  #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
             for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[b][kb][v]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -291,9 +300,9 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
         const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
         alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use);
         float sum = 0.f;
-  #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][kb][v], scale_log2, -m_use));
             s[b][kb][v] = e;
@@ -305,24 +314,24 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
         m_run[b] = m_new;
         // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j
         // (j<4) or 32st+16+4gp+(j-4), matching the V^T reads below
-  #pragma unroll
-        for (int st = 0; st < 2; ++st)
-  #pragma unroll
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
           for (int v = 0; v < 4; ++v) {
             pb[b][st][v] = (__bf16)s[b][2 * st][v];
             pb[b][st][4 + v] = (__bf16)s[b][2 * st + 1][v];
           }
       }
       if (__any(grew)) {
-  #pragma unroll
+#pragma unroll
         for (int b = 0; b < 2; ++b)
-  #pragma unroll
+#pragma unroll
           for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha[b];
       }
-  #pragma unroll
+#pragma unroll
       for (int mb = 0; mb < HD / 16; ++mb)
-  #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
           const int c = 2 * mb + (tc >> 1), h8 = (tc & 1) * 8;
           const int k1 = 32 * st + tkey, k2 = k1 + 16;
           const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -368,14 +377,18 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? 2 : 1) void attn_bf16_kernel(AttnA
 // Merge the key-split partials of one row in split order, for every head:
 // out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s over the splits that
 // hold keys of the row.  Rows of tiles that were not split are skipped.  One
-// workgroup per row: the per-(head, split) weights go to LDS first, then each
-// thread adds the splits of 4 consecutive dims of one head with independent
-// loads.
+// workgroup per (row, group of kMergeHeads heads): the per-(head, split)
+// weights go to LDS first, then each thread adds the splits of 4 consecutive
+// dims of one head with independent loads.
+constexpr int kMergeHeads = 8;
+
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  extern __shared__ float coef[];   // [n_q][ns]
+  extern __shared__ float coef[];   // [kMergeHeads][ns]
   __shared__ int s_pm;
   const int i = blockIdx.x;
+  const int h0 = blockIdx.y * kMergeHeads;
+  const int nh = min(kMergeHeads, a.n_q - h0);
   const int tid = threadIdx.x;
   // the attention workgroup of this row's tile decided whether to split
   const TileInfo ti = tile_info(a, tile_of_row(a, i));
@@ -395,31 +408,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   int p = a.qpos ? a.qpos[i] : i;
   p = p < 0 ? 0 : (p >= ti.T ? ti.T - 1 : p);
   const int ns = p / a.key_split + 1;
-  for (int head = tid; head < a.n_q; head += 256) {
+  if (tid < nh) {
+    const int head = h0 + tid;
     float m = -INFINITY;
     for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, a.ml_part[(((int64_t)sp * a.m + i) * a.n_q + head) * 2]);
     float den = 0.f;
     for (int sp = 0; sp < ns; ++sp) {
       const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + (((int64_t)sp * a.m + i) * a.n_q + head) * 2);
       const float wgt = exp2f(ml.x - m);
-      coef[head * ns + sp] = wgt;
+      coef[tid * ns + sp] = wgt;
       den += wgt * ml.y;
     }
     const float inv = 1.0f / den;
-    for (int sp = 0; sp < ns; ++sp) coef[head * ns + sp] *= inv;
+    for (int sp = 0; sp < ns; ++sp) coef[tid * ns + sp] *= inv;
   }
   __syncthreads();
   const int per_row = a.n_q * HD;
-  for (int c = tid * 4; c < per_row; c += 256 * 4) {
-    const int head = c / HD;
+  for (int c = tid * 4; c < nh * HD; c += 256 * 4) {
+    const int hl = c / HD, head = h0 + hl;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int sp = 0; sp < ns; ++sp) {
       const int64_t slot = ((int64_t)sp * a.m + i) * a.n_q + head;
-      const float wgt = coef[head * ns + sp];
+      const float wgt = coef[hl * ns + sp];
       const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + (c % HD));
       num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;
     }
-    bf16_t* Op = (bf16_t*)a.O + (int64_t)i * per_row + c;
+    bf16_t* Op = (bf16_t*)a.O + (int64_t)i * per_row + h0 * HD + c;
     const uint32_t w0 = (uint32_t)f2bf(num.x) | ((uint32_t)f2bf(num.y) << 16);
     const uint32_t w1 = (uint32_t)f2bf(num.z) | ((uint32_t)f2bf(num.w) << 16);
     *reinterpret_cast<uint2*>(Op) = make_uint2(w0, w1);
@@ -496,8 +510,8 @@ hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.key_split <= 0) return e;
   LaunchScope ls("attn_merge", s);
-  const size_t coef_bytes = (size_t)a.n_q * n_split * sizeof(float);
-  attn_merge_kernel<HD><<<a.m, 256, coef_bytes, s>>>(a);
+  const size_t coef_bytes = (size_t)kMergeHeads * n_split * sizeof(float);
+  attn_merge_kernel<HD><<<dim3(a.m, (a.n_q + kMergeHeads - 1) / kMergeHeads), 256, coef_bytes, s>>>(a);
   return hipGetLastError();
 }
 
