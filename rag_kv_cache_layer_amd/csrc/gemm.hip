@@ -157,9 +157,10 @@ __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float*
                              int M, int N) {
   constexpr bool swiglu = KIND == EPI_SWIGLU;
   const int cols = swiglu ? bn / 2 : bn;
-  const int tpr = cols / 8;  // threads per row (power of two, <= 64)
+  const int tpr = cols / 8;  // threads per row (a power of two <= 64 for the QKV deviation reduction)
   const int rpp = NT / tpr;
   const int tid = threadIdx.x;
+  if (tid >= rpp * tpr) return;   // idle when tpr does not divide NT (224-wide tiles)
   const int lr = tid / tpr, lc = (tid % tpr) * 8;
   const bool want_dev = KIND == EPI_QKV && e.dev_part != nullptr;
   const int q_end = e.q_dim, k_end = e.q_dim + e.kv_dim;
@@ -386,30 +387,38 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel, large tile: 256x256 output, 8 waves of 128x64 (8x4 MFMA
-// blocks, accumulators in AGPRs, two waves per SIMD), K step 32 with a
+// bf16 MFMA kernel, large tile for the gate/up projection: 256 rows x LBN
+// columns (LBN/2 gate + LBN/2 up features) with 8 waves, K step 32 with a
 // 4-deep LDS ring.  The tile halves the L2-to-LDS bytes per flop of the
-// 128x128 kernel and each SIMD interleaves two waves' MFMA streams.  Used
-// where N is large (the gate/up projection).
+// 128x128 kernel.  LBN = 224 gives the 8B layer's 493 rows x 14336 features
+// 2 x 128 = 256 workgroups, one per CU (256 wide leaves 32 CUs idle); its
+// waves are 4 (M) x 2 (N) of 64x112 (4x7 MFMA blocks); LBN = 256 uses
+// 2 x 4 waves of 128x64.
 // ---------------------------------------------------------------------------
-#ifndef CB_BIG_BK
-#define CB_BIG_BK 32
+#ifndef CB_BIG_BN
+#define CB_BIG_BN 256
+#endif
+#ifndef CB_BIG_WAVES
+#define CB_BIG_WAVES 8
 #endif
 #ifndef CB_BIG_NSTAGE
-#define CB_BIG_NSTAGE (CB_BIG_BK == 32 ? 4 : 2)
+#define CB_BIG_NSTAGE 4
 #endif
-#ifndef CB_BIG_ILV
-#define CB_BIG_ILV 1
-#endif
-#ifndef CB_BIG_ILV_PER
-#define CB_BIG_ILV_PER 0   // MFMA rows between DMA groups (0: spread over the step)
-#endif
-constexpr int LBM = 256, LBN = 256, LBK = CB_BIG_BK, LNS = CB_BIG_NSTAGE, LCLD = LBN + 4;
-constexpr int kLStage = (LBM + LBN) * LBK * 2;                         // 32 or 64 KB
+constexpr int LBM = 256, LBN = CB_BIG_BN, LBK = 32, LNS = CB_BIG_NSTAGE, LCLD = LBN + 4;
+constexpr int kLW = CB_BIG_WAVES;                    // waves per workgroup
+static_assert(LBN == 224 || LBN == 256, "large tile: 224 or 256 columns");
+static_assert(kLW == 8 || (kLW == 4 && LBN == 256), "8 waves, or 4 waves of 128x128");
+static_assert(LNS >= 2 && LNS <= 4, "ring depth");
+constexpr int kLNT = 64 * kLW;
+constexpr int kLWN = kLW == 4 ? 2 : (LBN == 224 ? 2 : 4);   // waves along N
+constexpr int kLWTM = LBM / (kLW / kLWN);            // wave tile rows (64 or 128)
+constexpr int kLWTN = LBN / kLWN;                    // wave tile columns (112, 64 or 128)
+constexpr int kLFA = kLWTM / 16, kLFB = kLWTN / 16;  // MFMA blocks per wave
+constexpr int kLStage = (LBM + LBN) * LBK * 2;       // 30 or 32 KB
 constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LCLD * 4;
-static_assert(LBK == 32 || LBK == 64, "big tile: BK is 32 or 64");
-constexpr int kLRows = 1024 / (LBK * 2);       // rows one DMA instruction fills
-constexpr int kLGroups = LBM / kLRows / 8;     // row groups per operand per wave
+constexpr int kLBlocksA = LBM / 16, kLBlocks = (LBM + LBN) / 16;   // 1 KB blocks per stage
+constexpr int kLBPW = (kLBlocks + kLW - 1) / kLW;   // blocks per wave (at most)
+static_assert(kLBPW <= 8 && kLFA % kLBPW == 0, "blocks are issued between MFMA rows");
 
 // 64-byte rows (BK = 32) in 1 KB blocks of 16 rows.  Inside a block, row r
 // sits in row slot rho(r) and its 16-byte chunk c in slot c ^ ((r >> 1) & 3).
@@ -423,109 +432,103 @@ __device__ __forceinline__ int swz32(int r, int c) {
   const int rl = r & 15;
   return (r >> 4) * 1024 + rho16(rl) * 64 + ((c ^ ((rl >> 1) & 3)) << 4);
 }
-// byte offset of 16-byte chunk c of tile row r in a big-tile stage
-__device__ __forceinline__ int lswz(int r, int c) { return LBK == 32 ? swz32(r, c) : swz(r, c); }
+
+// s_waitcnt with the later steps' loads still allowed in flight (ps loads per
+// step, later <= 2 steps)
+#define CB_WAIT_LATER(ps, later)                 \
+  do {                                           \
+    if ((later) >= 2) CB_WAIT_VMCNT(2 * (ps));   \
+    else if ((later) == 1) CB_WAIT_VMCNT(ps);    \
+    else CB_WAIT_VMCNT(0);                       \
+  } while (0)
 
 template <int KIND>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int mt, int ntiles) {
+__global__ __launch_bounds__(kLNT, 1) void gemm_bf16_big_kernel(GemmArgs g, int mt, int ntiles) {
   __shared__ __attribute__((aligned(16))) char smem[kLSmem];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // 8 waves: 2 (M) x 4 (N)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int tm = id % mt, tn = id / mt;
   const int m0 = tm * LBM;
   const int M = g.M, K = g.K;
   const int nk = (K + LBK - 1) / LBK;
 
-  // DMA plan: a wave instruction fills one 1 KB block (16 rows x 64 B or
-  // 8 rows x 128 B); wave w moves row groups w*kLGroups + j of A and of B.
+  // DMA plan: a wave instruction fills one 1 KB block of 16 rows x 64 B;
+  // wave w moves blocks w, w + kLW, w + 2 kLW, ... of the stage (A's blocks
+  // first, then B's).
   const uint32_t kOOB = 0x80000000u;
-  __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
-  __amdgpu_buffer_rsrc_t rb[kLGroups];
-  uint32_t aoff[kLGroups], boff[kLGroups];
-  int lcol[kLGroups];
+  const int nbw = (kLBlocks - w + kLW - 1) / kLW;   // blocks of this wave (uniform)
+  const int rl = rho16_inv(lane >> 2);      // the row whose slot this lane fills
+  const int lcol = ((lane & 3) ^ ((rl >> 1) & 3)) * 8;
+  __amdgpu_buffer_rsrc_t rs[kLBPW];
+  uint32_t off[kLBPW];
+  int dst[kLBPW];
 #pragma unroll
-  for (int j = 0; j < kLGroups; ++j) {
-    const int grp = w * kLGroups + j;
-    int rl, ch;   // the row and the chunk whose slot this lane fills
-    if (LBK == 32) {
-      rl = rho16_inv(lane >> 2);
-      ch = (lane & 3) ^ ((rl >> 1) & 3);
+  for (int j = 0; j < kLBPW; ++j) {
+    const int blk = min(w + kLW * j, kLBlocks - 1);
+    if (blk < kLBlocksA) {
+      const int row = blk * 16 + rl;
+      rs[j] = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
+      off[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
+      dst[j] = blk * 1024;
     } else {
-      rl = lane >> 3;
-      ch = (lane & 7) ^ (((grp * 8 + rl) >> 1) & 7);
+      const int r0 = (blk - kLBlocksA) * 16;
+      const void* base;
+      int brow, nrows;
+      if (g.B.mode == 0) {
+        const int c0 = tn * LBN + r0;
+        if (c0 < g.B.n1) { base = g.B.p0; brow = c0; nrows = g.B.n1; }
+        else if (c0 < g.B.n2) { base = g.B.p1; brow = c0 - g.B.n1; nrows = g.B.n2 - g.B.n1; }
+        else { base = g.B.p2; brow = c0 - g.B.n2; nrows = g.N - g.B.n2; }
+      } else {
+        base = r0 < LBN / 2 ? g.B.p0 : g.B.p1;
+        brow = tn * (LBN / 2) + (r0 % (LBN / 2));
+        nrows = g.B.n_feat;
+      }
+      rs[j] = make_rsrc(base, (uint32_t)((int64_t)(nrows > 0 ? nrows : 0) * K * 2));
+      const int myrow = brow + rl;
+      off[j] = myrow < nrows ? (uint32_t)((int64_t)myrow * K * 2) : kOOB;
+      dst[j] = blk * 1024;   // B's blocks follow A's in the stage
     }
-    const int row = grp * kLRows + rl;
-    lcol[j] = ch * 8;
-    aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
-    const int r0 = grp * kLRows;
-    const void* base;
-    int brow, nrows;
-    if (g.B.mode == 0) {
-      const int c0 = tn * LBN + r0;
-      if (c0 < g.B.n1) { base = g.B.p0; brow = c0; nrows = g.B.n1; }
-      else if (c0 < g.B.n2) { base = g.B.p1; brow = c0 - g.B.n1; nrows = g.B.n2 - g.B.n1; }
-      else { base = g.B.p2; brow = c0 - g.B.n2; nrows = g.N - g.B.n2; }
-    } else {
-      base = r0 < LBN / 2 ? g.B.p0 : g.B.p1;
-      brow = tn * (LBN / 2) + (r0 % (LBN / 2));
-      nrows = g.B.n_feat;
-    }
-    rb[j] = make_rsrc(base, (uint32_t)((int64_t)(nrows > 0 ? nrows : 0) * K * 2));
-    const int myrow = brow + rl;
-    boff[j] = myrow < nrows ? (uint32_t)((int64_t)myrow * K * 2) : kOOB;
   }
   auto issue_group = [&](int stage, int k0, int j) {
-    char* sa = smem + stage * kLStage;
-    char* sb = sa + LBM * LBK * 2;
-    const int grp = w * kLGroups + j;
-    const int kk = k0 + lcol[j];
-    const bool kin = kk < K;
-    const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
-    const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+    if (j >= nbw) return;
+    const int kk = k0 + lcol;
+    const uint32_t o = (kk < K && off[j] != kOOB) ? off[j] + kk * 2 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kLStage + dst[j]), 16, o, 0, 0, 0);
   };
   auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int j = 0; j < kLGroups; ++j) issue_group(stage, k0, j);
+    for (int j = 0; j < kLBPW; ++j) issue_group(stage, k0, j);
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[kLFA][kLFB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kLFA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int wm = (w >> 2) * 128, wn = (w & 3) * 64;
+    for (int j = 0; j < kLFB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = (w / kLWN) * kLWTM, wn = (w % kLWN) * kLWTN;
   const int fr = lane & 15, fc = lane >> 4;
-  // one step's MFMAs; with CB_BIG_ILV the next stage's DMA (when nstage >= 0)
-  // is issued a group at a time between them instead of in one burst
+  // one step's MFMAs, with the next stage's loads (nstage >= 0) issued one
+  // block at a time between the MFMA rows instead of in one burst
   auto compute = [&](int stage, int nstage, int nk0) {
     const char* sa = smem + stage * kLStage;
     const char* sb = sa + LBM * LBK * 2;
+    bf16x8_t af[kLFA], bfr[kLFB];
 #pragma unroll
-    for (int ks = 0; ks < LBK / 32; ++ks) {
-      bf16x8_t af[8], bfr[4];
+    for (int i = 0; i < kLFA; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + lswz(wm + i * 16 + fr, ks * 4 + fc));
+    for (int j = 0; j < kLFB; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + j * 16 + fr, fc));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + lswz(wn + j * 16 + fr, ks * 4 + fc));
+    for (int i = 0; i < kLFA; ++i) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-#if CB_BIG_ILV
-        constexpr int per = CB_BIG_ILV_PER > 0 ? CB_BIG_ILV_PER : 8 * (LBK / 32) / kLGroups;
-        const int slot = ks * 8 + i;
-        if (nstage >= 0 && slot % per == per - 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          issue_group(nstage, nk0, slot / per);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#endif
+      for (int j = 0; j < kLFB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      constexpr int per = kLFA / kLBPW;   // MFMA rows between issued blocks
+      if (nstage >= 0 && i % per == per - 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_group(nstage, nk0, i / per);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -539,21 +542,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
       const int it = it0 + u;
       if (it < nk) {
         // this wave's step `it` landed once at most the later steps' loads
-        // (2 kLGroups per step) are outstanding
+        // (nbw per step) are outstanding; then every wave's have (barrier)
         const int later = min(nk - 1 - it, LNS - 2);
-        constexpr int PS = 2 * kLGroups;
-        if (later >= 3) CB_WAIT_VMCNT(3 * PS);
-        else if (later == 2) CB_WAIT_VMCNT(2 * PS);
-        else if (later == 1) CB_WAIT_VMCNT(PS);
-        else CB_WAIT_VMCNT(0);
+        if (nbw == kLBPW) CB_WAIT_LATER(kLBPW, later);
+        else CB_WAIT_LATER(kLBPW - 1, later);
         CB_BARRIER();
         const bool more = it + LNS - 1 < nk;
-#if CB_BIG_ILV
         compute(u, more ? (u + LNS - 1) % LNS : -1, (it + LNS - 1) * LBK);
-#else
-        if (more) issue((u + LNS - 1) % LNS, (it + LNS - 1) * LBK);
-        compute(u, -1, 0);
-#endif
       }
     }
   }
@@ -564,16 +559,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(GemmArgs g, int m
   float* Cs = (float*)smem;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if ((w >> 2) == half) {
+    if (wm / 128 == half) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kLFA; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kLFB; ++j)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) Cs[(i * 16 + fc * 4 + v) * LCLD + wn + j * 16 + fr] = acc[i][j][v];
+          for (int v = 0; v < 4; ++v)
+            Cs[(wm - half * 128 + i * 16 + fc * 4 + v) * LCLD + wn + j * 16 + fr] = acc[i][j][v];
     }
     __syncthreads();
-    run_epilogue<bf16_t, 128, LBN, 512, KIND>(g.epi, g.B, Cs, LCLD, m0 + half * 128, tn, M, g.N);
+    run_epilogue<bf16_t, 128, LBN, kLNT, KIND>(g.epi, g.B, Cs, LCLD, m0 + half * 128, tn, M, g.N);
     __syncthreads();
   }
 }
@@ -727,7 +723,7 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
     g.N = nt * LBN;
     g.splits = 1;
     LaunchScope ls("gemm_gateup", s);
-    gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), 512, 0, s>>>(g, mt, nt);
+    gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), kLNT, 0, s>>>(g, mt, nt);
     return hipGetLastError();
   }
   const int ntiles = gemm_n_tiles(dtype, g.B, g.N);
