@@ -226,6 +226,7 @@ def main():
             F.full_prefill_layer(cfg, layer, rope, h_full, T, 0, kf, vf, h2, ws)
         torch.cuda.synchronize()
         extra["full_prefill_ms"] = round((time.perf_counter() - t0) * 100, 4)
+        extra["shift_stack"] = shift_stack_measure()
 
     if args.batch > 1:
         # n_req requests of the same shape (own caches, same rows): one shift
@@ -307,6 +308,50 @@ def main():
     }
     out.update(extra)
     print(json.dumps(out))
+
+
+def shift_stack_measure(reps=6):
+    """cb_rope_shift over a whole 32-layer 8B stack's key cache (8 x 512 + 64
+    tokens: 3584 shifted rows per layer), one launch per call, alternating
+    between two caches of 272 MB each so that no call finds its data in the
+    256 MB Infinity Cache.  Algorithmic bytes: every shifted element is read
+    and written once."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+    p = synth.PRESETS["llama8b_stack"]
+    cfg = F.config_of(p)
+    offs = synth.chunk_offsets(p, range(p.n_chunks))
+    T, kvd, L = p.T, p.kv_dim, p.n_layers
+    rope = F.DeviceRope(cfg, T)
+    bufs = [torch.randn((L, T, kvd), device="cuda").to(torch.bfloat16) for _ in range(2)]
+    F.rope_shift(cfg, rope, bufs[0], T * kvd, L, T, offs)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        F.rope_shift(cfg, rope, bufs[i % 2], T * kvd, L, T, offs)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    nbytes = 2 * L * (p.n_ctx - int(offs[1])) * kvd * 2
+    # reference: a device-to-device copy moving the same bytes (read + write)
+    src = bufs[0].view(-1)[: nbytes // 4]
+    dst = bufs[1].view(-1)[: nbytes // 4]
+    ctimes = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ctimes.append(e0.elapsed_time(e1))
+    cms = sorted(ctimes)[len(ctimes) // 2]
+    return {"layers": L, "bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "copy_same_bytes_gbs": round(nbytes / (cms * 1e-3) / 1e9, 1)}
 
 
 def pipeline_measure(seed, reps=3):
