@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--pipeline", action="store_true",
                     help="also measure the 32-layer stack with its KV loaded from pinned host memory "
                          "(loading alone, recompute alone, both pipelined)")
+    ap.add_argument("--analytics", action="store_true",
+                    help="also run the deviation analytics (attention deviation vs r, deviation "
+                         "concentration, neighbour-layer rank correlation) on the 32-layer stack")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 512 MiB device-to-device copy first (a known-size reference "
                          "for the HBM byte counters)")
@@ -274,6 +277,8 @@ def main():
                           "kernels": bk}
     if args.pipeline:
         extra["pipeline"] = pipeline_measure(seed)
+    if args.analytics:
+        extra["analytics"] = analytics_measure(seed)
 
     cpu = None
     log(f"gpu timing done: {ms:.4f} ms/step")
@@ -436,6 +441,45 @@ def pipeline_measure(seed, reps=3):
             "hidden_fraction": round((t_load + t_comp - t_pipe) / min(t_load, t_comp), 3),
             "pcie_inclusive_tokens_per_s": round(T / t_pipe, 1),
             "full_prefill_layer_ms": round(t_pf * 1e3, 4), "controller_r_e4": r_e4}
+
+
+def analytics_measure(seed):
+    """Deviation analytics of the 32-layer 8B stack (8 x 512 + 64 tokens) with
+    seeded N(0, 0.02) weights drawn on the device and N(0, 1) embeddings; the
+    chunk caches come from each chunk's isolated prefill through the stack."""
+    import torch
+    from rag_kv_cache_layer_amd import analytics as GA
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+    p = synth.PRESETS["llama8b_stack"]
+    cfg = F.config_of(p)
+    log("analytics: generating the 32-layer stack on the device")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2000 + seed)
+    shapes = {"w_q": (p.q_dim, p.d_model), "w_k": (p.kv_dim, p.d_model), "w_v": (p.kv_dim, p.d_model),
+              "w_o": (p.d_model, p.q_dim), "w_gate": (p.ffn_dim, p.d_model), "w_up": (p.ffn_dim, p.d_model),
+              "w_down": (p.d_model, p.ffn_dim)}
+    layers = []
+    for _ in range(p.n_layers):
+        w = {n: (torch.randn(s, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for n, s in shapes.items()}
+        w["attn_norm"] = torch.ones(p.d_model, device="cuda")
+        w["mlp_norm"] = torch.ones(p.d_model, device="cuda")
+        layers.append(F.DeviceLayer(cfg, w))
+        del w
+    offs = synth.chunk_offsets(p, range(p.n_chunks))
+    x_all = torch.randn((p.T, p.d_model), generator=g, device="cuda").to(torch.bfloat16)
+    rope = F.DeviceRope(cfg, p.T)
+    t0 = time.perf_counter()
+    out = GA.stack_study(cfg, layers, rope, x_all, offs, [0, 500, 1000, 1500, 3000, 10000])
+    torch.cuda.synchronize()
+    ts = out["top_share"]
+    return {"workload": "llama8b_stack: 32 layers, 8x512-token chunks + 64-token query (T=4160)",
+            "ratios": [r / 1e4 for r in out["ratios_e4"]],
+            "attn_dev_rel_mean": [round(x, 6) for x in out["attn_dev_mean"]],
+            "top_share_mean_layers_1plus": {f: round(sum(v[1:]) / (len(v) - 1), 4) for f, v in ts.items()},
+            "spearman_neighbours_mean": round(sum(out["spearman_neighbours"]) / len(out["spearman_neighbours"]), 4),
+            "spearman_neighbours_min": round(min(out["spearman_neighbours"]), 4),
+            "seconds": round(time.perf_counter() - t0, 2)}
 
 
 def cpu_baseline(p, seed, k, budget_s):
