@@ -287,6 +287,32 @@ cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_weights* w,
                          float* dev_out, int32_t* s_out, int32_t* m_out_host, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* 8-bit float operands (the paper serves its larger models with 8-bit
+ * weights, section 7): OCP fp8 E4M3 codes (bias 7, largest finite 448, no
+ * infinities) with one power-of-two scale per row.
+ *
+ * cb_quantize_fp8: x device [rows][cols] (src_dtype CB_F32 or CB_BF16) ->
+ * codes device uint8 [rows][cols] and exps device int32 [rows], where
+ * exps[i] is the smallest integer e with max_j |x[i][j]| <= 448 * 2^e (0 for
+ * an all-zero row) and codes[i][j] is x[i][j] * 2^-e (exact) clamped to +-448
+ * and rounded to the nearest E4M3 value, ties to even. */
+cb_status cb_quantize_fp8(int32_t src_dtype, const void* x, int32_t rows, int32_t cols,
+                          uint8_t* codes, int32_t* exps, void* stream);
+
+/* Bytes of workspace cb_gemm_fp8 needs for these sizes (0 = none). */
+size_t cb_gemm_fp8_workspace_size(int32_t M, int32_t N, int32_t K);
+
+/* C[i][j] = sum_k A[i][k] B[j][k] * 2^(a_exp[i] + b_exp[j]) for E4M3 codes A
+ * device [M][K] and B device [N][K] (nn.Linear layout), row exponents as
+ * produced by cb_quantize_fp8; products are exact and accumulate in fp32.
+ * c device [M][ldc] (out_dtype CB_F32 or CB_BF16, rounded once).  K must be a
+ * multiple of 16 and A, B 16-byte aligned (CB_ERR_SHAPE); M*K and N*K below
+ * 2^31 (CB_ERR_UNSUPPORTED).  ws: device, >= cb_gemm_fp8_workspace_size
+ * bytes (may be NULL when that is 0). */
+cb_status cb_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* a, const int32_t* a_exp,
+                      const uint8_t* b, const int32_t* b_exp, void* c, int32_t ldc, int32_t out_dtype,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* The fusor over a stack of n_layers layers (section 4.3, Figure 9), with
  * each layer's KV loaded while the previous layer is recomputed (section 5,
  * Figure 11: the fusor waits for the previous layer's recompute and for the

@@ -944,3 +944,48 @@ extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_w
   // 5. O projection, MLP over all kept rows (residual rows via the selection)
   return layer_tail(c, *w, L, ws, M_out, hidden_in, M_in, at<int>(ws, L.sel), nullptr, hidden_out, s);
 }
+
+// ---------------------------------------------------------------------------
+// fp8 E4M3 operands
+// ---------------------------------------------------------------------------
+
+extern "C" cb_status cb_quantize_fp8(int32_t src_dtype, const void* x, int32_t rows, int32_t cols, uint8_t* codes,
+                                     int32_t* exps, void* stream) {
+  if (src_dtype != CB_F32 && src_dtype != CB_BF16) return CB_ERR_ARG;
+  if (rows < 0 || cols < 0 || (rows > 0 && (!x || !codes || !exps))) return CB_ERR_ARG;
+  if (rows == 0 || cols == 0) return CB_OK;
+  return hip_status(launch_quantize_rows(src_dtype, x, rows, cols, codes, exps, (hipStream_t)stream));
+}
+
+extern "C" size_t cb_gemm_fp8_workspace_size(int32_t M, int32_t N, int32_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  const int s = fp8_splits(N, K);
+  return s > 1 ? (size_t)s * M * N * 4 : 0;
+}
+
+extern "C" cb_status cb_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* a, const int32_t* a_exp,
+                                 const uint8_t* b, const int32_t* b_exp, void* c, int32_t ldc, int32_t out_dtype,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || ldc < N) return CB_ERR_ARG;
+  if (out_dtype != CB_F32 && out_dtype != CB_BF16) return CB_ERR_ARG;
+  if (M == 0 || N == 0) return CB_OK;
+  if (!a || !a_exp || !b || !b_exp || !c) return CB_ERR_ARG;
+  if (K % 16 || !aligned16(a) || !aligned16(b)) return CB_ERR_SHAPE;
+  if ((int64_t)M * K >= (int64_t)1 << 31 || (int64_t)N * K >= (int64_t)1 << 31) return CB_ERR_UNSUPPORTED;
+  Fp8GemmArgs g{};
+  g.A = a;
+  g.a_exp = a_exp;
+  g.B = b;
+  g.b_exp = b_exp;
+  g.C = c;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ldc = ldc;
+  g.splits = fp8_splits(N, K);
+  if (g.splits > 1) {
+    if (!ws || ws_bytes < cb_gemm_fp8_workspace_size(M, N, K)) return CB_ERR_WORKSPACE;
+    g.part = (float*)ws;
+  }
+  return hip_status(launch_gemm_fp8(g, out_dtype, (hipStream_t)stream));
+}

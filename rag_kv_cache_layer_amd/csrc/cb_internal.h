@@ -236,6 +236,24 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
 // ---------------------------------------------------------------------------
 // Attention of selected rows over the cache.
 // ---------------------------------------------------------------------------
+// fp8 E4M3 operands with one power-of-two scale per row:
+// C[i][j] = sum_k A[i][k] B[j][k] * 2^(a_exp[i] + b_exp[j]); A [M][K], B [N][K]
+// row-major codes; C [M][ldc] in the output dtype.
+struct Fp8GemmArgs {
+  const uint8_t* A;
+  const int* a_exp;
+  const uint8_t* B;
+  const int* b_exp;
+  void* C;
+  int M, N, K, ldc;
+  int splits;     // split-K factor (fp32 partials in part, summed in order)
+  float* part;    // [splits][M][N]
+};
+int fp8_splits(int N, int K);
+hipError_t launch_quantize_rows(int src_dtype, const void* x, int rows, int cols, uint8_t* q, int* ex,
+                                hipStream_t s);
+hipError_t launch_gemm_fp8(const Fp8GemmArgs& g, int out_dtype, hipStream_t s);
+
 constexpr int kAttnRowTile = 32;   // kept rows per attention workgroup (one row tile)
 
 struct AttnArgs {

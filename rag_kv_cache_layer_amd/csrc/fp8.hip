@@ -1,0 +1,238 @@
+// 8-bit float operands for the projections (the paper serves its larger
+// models with 8-bit weights, CacheBlend section 7): OCP fp8 E4M3 with one
+// power-of-two scale per matrix row.
+//
+// quantize_rows_kernel: one workgroup per row.  e = the smallest integer with
+// amax <= 448 * 2^e, found from the bits of amax (amax = m * 2^E, m in [1,2):
+// e = E - 8 + (m > 1.75)); every element is scaled by 2^-e (exact), clamped
+// to +-448 and rounded to the nearest E4M3 value, ties to even
+// (v_cvt_pk_fp8_f32).
+//
+// gemm_fp8_kernel: C = (A B^T) * 2^(e_a[row] + e_b[col]) for fp8 A [M][K] and
+// B [N][K].  128x128 tiles, 4 waves of 64x64 built from
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit block scales; every
+// product is exact in fp32).  K steps of 128 bytes: a row step is 128 bytes
+// as in the bf16 kernel's 64-element steps, so the same direct-to-LDS ring
+// and XOR swizzle serve, and each MFMA takes two adjacent 16-byte chunks of
+// a row.  The K index of an MFMA is a sum, so any assignment of a row's 128
+// bytes to lanes that A and B share gives the same product.  Split-K
+// partials are scaled before they are written (exact) and summed in split
+// order.
+#include "cb_internal.h"
+
+namespace cb {
+
+namespace {
+
+constexpr int QBM = 128, QBN = 128, QBK = 128, QNS = 3, QCLD = QBN + 4;
+constexpr int kQStage = (QBM + QBN) * QBK;                   // 32 KB
+constexpr int kQSmem = QNS * kQStage > QBM * QCLD * 4 ? QNS * kQStage : QBM * QCLD * 4;
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int qswz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ int row_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float m = 2.f * frexpf(amax, &E);   // amax = m * 2^(E-1), m in [1, 2)
+  return (E - 1) - 8 + (m > 1.75f ? 1 : 0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, int cols,
+                                                            uint8_t* __restrict__ q, int* __restrict__ ex) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const T* xr = x + (int64_t)row * cols;
+  float amax = 0.f;
+  for (int c = tid; c < cols; c += 256) amax = fmaxf(amax, fabsf(Elem<T>::ld(xr + c)));
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e = row_exponent(amax);
+  if (tid == 0) ex[row] = e;
+  uint8_t* qr = q + (int64_t)row * cols;
+  for (int c = 2 * tid; c < cols; c += 512) {
+    const float a = fminf(fmaxf(ldexpf(Elem<T>::ld(xr + c), -e), -448.f), 448.f);
+    const float b = c + 1 < cols ? fminf(fmaxf(ldexpf(Elem<T>::ld(xr + c + 1), -e), -448.f), 448.f) : 0.f;
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    qr[c] = (uint8_t)(pk & 0xff);
+    if (c + 1 < cols) qr[c + 1] = (uint8_t)((pk >> 8) & 0xff);
+  }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt, int ntiles) {
+  __shared__ __attribute__((aligned(16))) char smem[kQSmem];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = (gridDim.x & 7) == 0 ? ((int)blockIdx.x & 7) * (gridDim.x >> 3) + ((int)blockIdx.x >> 3)
+                                      : (int)blockIdx.x;
+  const int tm = id % mt, tn = id / mt;
+  const int m0 = tm * QBM, n0 = tn * QBN;
+  const int M = g.M, N = g.N, K = g.K;
+  const int kchunk = ((K + g.splits - 1) / g.splits + QBK - 1) / QBK * QBK;
+  const int kb = blockIdx.y * kchunk;
+  const int ke = min(K, kb + kchunk);
+  const int nk = ke > kb ? (ke - kb + QBK - 1) / QBK : 0;
+
+  // DMA plan (as the bf16 128x128 kernel): wave w fills row groups
+  // (w*4 + j)*8 .. +7 of the A and B tiles; lane i fills slot i%8 of row i/8
+  // with the logical chunk slot ^ ((row >> 1) & 7); out-of-range rows and K
+  // past ke load as zero.
+  const uint32_t kOOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)N * K));
+  uint32_t aoff[4], boff[4];
+  int lcol[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (w * 4 + j) * 8 + (lane >> 3);
+    lcol[j] = ((lane & 7) ^ ((row >> 1) & 7)) * 16;
+    aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K) : kOOB;
+    boff[j] = n0 + row < N ? (uint32_t)((int64_t)(n0 + row) * K) : kOOB;
+  }
+  auto issue = [&](int stage, int k0) {
+    char* sa = smem + stage * kQStage;
+    char* sb = sa + QBM * QBK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int grp = w * 4 + j;
+      const int kk = k0 + lcol[j];
+      const bool kin = kk < ke;
+      const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk : kOOB;
+      const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int fr = lane & 15, fc = lane >> 4;   // lane group fc takes chunks 2fc, 2fc+1 of the row
+  auto frag = [&](const char* base, int r) {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + qswz(r, 2 * fc));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + qswz(r, 2 * fc + 1));
+    return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto compute = [&](int stage) {
+    const char* sa = smem + stage * kQStage;
+    const char* sb = sa + QBM * QBK;
+    i32x8_t af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = frag(sa, wm + i * 16 + fr);
+      bfr[i] = frag(sb, wn + i * 16 + fr);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0,
+                                                                      127);
+  };
+
+#pragma unroll
+  for (int st = 0; st < QNS - 1; ++st)
+    if (st < nk) issue(st, kb + st * QBK);
+  for (int it0 = 0; it0 < nk; it0 += QNS) {
+#pragma unroll
+    for (int u = 0; u < QNS; ++u) {
+      const int it = it0 + u;
+      if (it < nk) {
+        if (it + 1 < nk) CB_WAIT_VMCNT(8 * (QNS - 2));
+        else CB_WAIT_VMCNT(0);
+        CB_BARRIER();
+        if (it + QNS - 1 < nk) issue((u + QNS - 1) % QNS, kb + (it + QNS - 1) * QBK);
+        compute(u);
+      }
+    }
+  }
+  CB_WAIT_VMCNT(0);
+  __syncthreads();
+
+  // scale by 2^(e_a + e_b) (exact) and write through an fp32 tile in LDS
+  float* Cs = (float*)smem;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn + j * 16 + fr;
+      const int eb = col < N ? g.b_exp[col] : 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm + i * 16 + fc * 4 + v;
+        const int ea = row < M ? g.a_exp[row] : 0;
+        Cs[(wm + i * 16 + fc * 4 + v) * QCLD + wn + j * 16 + fr] = ldexpf(acc[i][j][v], ea + eb);
+      }
+    }
+  __syncthreads();
+  if (g.splits > 1) {
+    float* P = g.part + (int64_t)blockIdx.y * M * N;
+    for (int idx = tid; idx < QBM * QBN; idx += 256) {
+      const int r = idx / QBN, c = idx % QBN;
+      if (m0 + r < M && n0 + c < N) P[(int64_t)(m0 + r) * N + n0 + c] = Cs[r * QCLD + c];
+    }
+    return;
+  }
+  for (int idx = tid; idx < QBM * QBN; idx += 256) {
+    const int r = idx / QBN, c = idx % QBN;
+    if (m0 + r < M && n0 + c < N) Elem<TO>::st((TO*)g.C + (int64_t)(m0 + r) * g.ldc + n0 + c, Cs[r * QCLD + c]);
+  }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(256) void fp8_split_sum_kernel(Fp8GemmArgs g) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)g.M * g.N) return;
+  float s = 0.f;
+  for (int sp = 0; sp < g.splits; ++sp) s += g.part[(int64_t)sp * g.M * g.N + i];
+  const int64_t r = i / g.N, c = i % g.N;
+  Elem<TO>::st((TO*)g.C + r * g.ldc + c, s);
+}
+
+}  // namespace
+
+int fp8_splits(int N, int K) {
+  const int nt = (N + QBN - 1) / QBN;
+  int s = 1;
+  while (s < 4 && nt * s < 48 && K / (2 * s) >= 1024) s *= 2;
+  return s;
+}
+
+hipError_t launch_quantize_rows(int src_dtype, const void* x, int rows, int cols, uint8_t* q, int* ex,
+                                hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  LaunchScope ls("quantize_fp8", s);
+  if (src_dtype == CB_BF16)
+    quantize_rows_kernel<bf16_t><<<rows, 256, 0, s>>>((const bf16_t*)x, cols, q, ex);
+  else
+    quantize_rows_kernel<float><<<rows, 256, 0, s>>>((const float*)x, cols, q, ex);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const Fp8GemmArgs& g, int out_dtype, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  const int mt = (g.M + QBM - 1) / QBM, nt = (g.N + QBN - 1) / QBN;
+  const dim3 grid(mt * nt, g.splits);
+  {
+    LaunchScope ls("gemm_fp8", s);
+    if (out_dtype == CB_BF16) gemm_fp8_kernel<bf16_t><<<grid, 256, 0, s>>>(g, mt, nt);
+    else gemm_fp8_kernel<float><<<grid, 256, 0, s>>>(g, mt, nt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.splits <= 1) return e;
+  LaunchScope ls("gemm_fp8_split_sum", s);
+  const int64_t n = (int64_t)g.M * g.N;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (out_dtype == CB_BF16) fp8_split_sum_kernel<bf16_t><<<blocks, 256, 0, s>>>(g);
+  else fp8_split_sum_kernel<float><<<blocks, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace cb

@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
         "cb_full_prefill_layer": (I32, [CFG, W, R, P, I32, I32, P, P, P, P, SZ, P]),
         "cb_blend_batch": (I32, [CFG, W, R, I32, ctypes.POINTER(BlendRequest), P, P, P, P, P, I32P, P, SZ, P]),
         "cb_stack_workspace_size": (SZ, [CFG, I32]),
+        "cb_quantize_fp8": (I32, [I32, P, I32, I32, P, P, P]),
+        "cb_gemm_fp8_workspace_size": (SZ, [I32, I32, I32]),
+        "cb_gemm_fp8": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P, SZ, P]),
         "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
         "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
                                  P, P]),
@@ -459,4 +462,41 @@ def blend_stack_native(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: De
         oi += m_in[l]
         oo += m_out[l]
     out[-1]["y"] = y[:m_out[-1]]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# fp8 E4M3 operands
+# ---------------------------------------------------------------------------
+
+def quantize_fp8(x, codes=None, exps=None, stream=None):
+    """cb_quantize_fp8 of a device matrix x [rows][cols] (bf16 or fp32);
+    returns (codes uint8 [rows][cols], exps int32 [rows])."""
+    torch = _torch()
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if codes is None else codes
+    exps = torch.empty(rows, dtype=torch.int32, device=x.device) if exps is None else exps
+    src = CB_BF16 if x.dtype == torch.bfloat16 else CB_F32
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bf16 or fp32")
+    _check(lib().cb_quantize_fp8(src, _dptr(x, "x"), rows, cols, _dptr(codes, "codes", torch.uint8, rows * cols),
+                                 _dptr(exps, "exps", torch.int32, rows), _stream(stream)), "cb_quantize_fp8")
+    return codes, exps
+
+
+def gemm_fp8(a, a_exp, b, b_exp, out, ws=None, stream=None):
+    """cb_gemm_fp8: out [M][N] (bf16 or fp32) = (A B^T) scaled by the row
+    exponents; a [M][K], b [N][K] uint8 codes."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    need = int(lib().cb_gemm_fp8_workspace_size(M, N, K))
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=a.device)
+    od = CB_BF16 if out.dtype == torch.bfloat16 else CB_F32
+    _check(lib().cb_gemm_fp8(M, N, K, _dptr(a, "a", torch.uint8, M * K), _dptr(a_exp, "a_exp", torch.int32, M),
+                             _dptr(b, "b", torch.uint8, N * K), _dptr(b_exp, "b_exp", torch.int32, N),
+                             _dptr(out, "out", None, M * out.stride(0)), out.stride(0), od,
+                             _dptr(ws, "ws") if need else None, ws.numel() if need else 0, _stream(stream)),
+           "cb_gemm_fp8")
     return out

@@ -1,0 +1,75 @@
+"""Pins of the oracle's 8-bit float format (OCP E4M3) and row scaling (CPU).
+
+* The value table: 0, the smallest subnormal 2^-9, the smallest normal 2^-6,
+  1 = 0x38, 448 = 0x7E the largest, 0x7F and 0xFF not finite; the 254 finite
+  codes decode to distinct values apart from +-0.
+* Encoding: every finite code's value maps back to that code (exact values
+  round trip); values between two neighbours go to the nearer one; a value
+  halfway between two neighbours goes to the one with the even code; the sign
+  is kept.  Checked against a brute-force nearest search on random inputs.
+* Row exponents: amax <= 448 * 2^e and amax > 448 * 2^(e-1) (smallest e), for
+  random rows and for the edge cases amax = 448 * 2^k (exact fit) and just
+  above; an all-zero row gets 0.
+* The GEMM of quantized operands equals the brute-force sum of products of
+  the decoded values."""
+import numpy as np
+import pytest
+
+from oracle import fp8
+
+
+def test_value_table():
+    v = fp8.VALUES
+    assert v[0x00] == 0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.nanmax(v) == 448.0 and np.nanmin(v) == -448.0
+    finite = v[~np.isnan(v)]
+    assert len(finite) == 254 and len(np.unique(finite)) == 253   # +0 and -0
+
+
+def test_encode_round_trip_and_nearest():
+    codes = np.array([c for c in range(256) if not np.isnan(fp8.VALUES[c])], np.uint8)
+    back = fp8.encode(fp8.VALUES[codes])
+    assert np.array_equal(fp8.VALUES[back], fp8.VALUES[codes])
+    rng = np.random.default_rng(0)
+    y = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-1, 1, 4000) * 2.0 ** -5,
+                        rng.normal(0, 3, 4000)])
+    y = np.clip(y, -448, 448)
+    got = fp8.VALUES[fp8.encode(y)]
+    grid = np.unique(fp8.VALUES[~np.isnan(fp8.VALUES)])
+    d = np.abs(grid[None, :] - y[:, None])
+    assert np.all(np.abs(got - y) == d.min(axis=1))
+
+
+def test_ties_go_to_even_code():
+    grid = np.unique(fp8.VALUES[~np.isnan(fp8.VALUES)])
+    pos = grid[grid >= 0]
+    mids = (pos[:-1] + pos[1:]) / 2
+    c = fp8.encode(mids)
+    assert np.all((c & 1) == 0)
+    assert np.all(fp8.encode(-mids) == (c | 0x80))
+
+
+def test_row_exponents_smallest_fit():
+    rng = np.random.default_rng(1)
+    x = (rng.normal(size=(50, 33)) * np.exp(rng.uniform(-20, 20, (50, 1)))).astype(np.float32)
+    e = fp8.row_exponents(x)
+    amax = np.abs(x).max(1).astype(np.float64)
+    assert np.all(amax <= 448 * 2.0 ** e) and np.all(amax > 448 * 2.0 ** (e - 1))
+    edge = np.array([[448.0], [896.0], [np.nextafter(np.float32(448.0), np.float32(1e9))], [0.0], [1.0]], np.float32)
+    assert list(fp8.row_exponents(edge)) == [0, 1, 1, 0, -8]
+
+
+def test_quantized_gemm_is_the_sum_of_decoded_products():
+    rng = np.random.default_rng(2)
+    a = rng.normal(size=(3, 40)).astype(np.float32)
+    b = rng.normal(size=(5, 40)).astype(np.float32) * 0.02
+    qa, ea = fp8.quantize_rows(a)
+    qb, eb = fp8.quantize_rows(b)
+    c = fp8.gemm(qa, ea, qb, eb)
+    for i in range(3):
+        for j in range(5):
+            s = sum(fp8.VALUES[qa[i, k]] * 2.0 ** ea[i] * fp8.VALUES[qb[j, k]] * 2.0 ** eb[j] for k in range(40))
+            assert c[i, j] == pytest.approx(s, rel=1e-12, abs=1e-15)
+    # the quantization error is within half a quantum of each value's binade
+    assert np.max(np.abs(fp8.dequantize_rows(qa, ea) - a) / np.abs(a).max(1, keepdims=True)) <= 2.0 ** -4
