@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--pipeline", action="store_true",
                     help="also measure the 32-layer stack with its KV loaded from pinned host memory "
                          "(loading alone, recompute alone, both pipelined)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time the layer's four projections with fp8 E4M3 operands (cb_quantize_fp8 + "
+                         "cb_gemm_fp8) at the same row count")
     ap.add_argument("--analytics", action="store_true",
                     help="also run the deviation analytics (attention deviation vs r, deviation "
                          "concentration, neighbour-layer rank correlation) on the 32-layer stack")
@@ -279,6 +282,8 @@ def main():
         extra["pipeline"] = pipeline_measure(seed)
     if args.analytics:
         extra["analytics"] = analytics_measure(seed)
+    if args.fp8:
+        extra["fp8"] = fp8_measure(p, m, args.steps)
 
     cpu = None
     log(f"gpu timing done: {ms:.4f} ms/step")
@@ -480,6 +485,52 @@ def analytics_measure(seed):
             "spearman_neighbours_mean": round(sum(out["spearman_neighbours"]) / len(out["spearman_neighbours"]), 4),
             "spearman_neighbours_min": round(min(out["spearman_neighbours"]), 4),
             "seconds": round(time.perf_counter() - t0, 2)}
+
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
+
+
+def fp8_measure(p, m, steps):
+    """The four projections of the 8B layer at m rows with fp8 E4M3 operands:
+    weights quantized once (untimed), each activation matrix quantized per
+    row inside the timed call (cb_quantize_fp8 + cb_gemm_fp8, bf16 out)."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    d, q, kv, ffn = p.d_model, p.q_dim, p.kv_dim, p.ffn_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3000)
+    shapes = {"qkv": (q + 2 * kv, d), "o": (d, q), "gateup": (2 * ffn, d), "down": (d, ffn)}
+    out = {}
+    for name, (N, K) in shapes.items():
+        w = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        qw, ew = F.quantize_fp8(w)
+        del w
+        x = torch.randn((m, K), generator=g, device="cuda").to(torch.bfloat16)
+        qx = torch.empty((m, K), dtype=torch.uint8, device="cuda")
+        ex = torch.empty(m, dtype=torch.int32, device="cuda")
+        y = torch.empty((m, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(int(F.lib().cb_gemm_fp8_workspace_size(m, N, K)), 1), dtype=torch.uint8, device="cuda")
+
+        def call():
+            F.quantize_fp8(x, qx, ex)
+            F.gemm_fp8(qx, ex, qw, ew, y, ws)
+
+        for _ in range(5):
+            call()
+        F.profile_begin()
+        for _ in range(steps):
+            call()
+        st = F.profile_end()
+        torch.cuda.synchronize()
+        gm = st["gemm_fp8"]["total_ms"] / st["gemm_fp8"]["launches"]
+        if "gemm_fp8_split_sum" in st:
+            gm += st["gemm_fp8_split_sum"]["total_ms"] / st["gemm_fp8_split_sum"]["launches"]
+        qm = st["quantize_fp8"]["total_ms"] / st["quantize_fp8"]["launches"]
+        tf = 2 * m * N * K / (gm * 1e-3) / 1e12
+        out[name] = {"gemm_ms": round(gm, 5), "quantize_ms": round(qm, 5), "tflops": round(tf, 1),
+                     "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del qw, ew, x, qx, y, ws
+    return out
 
 
 def cpu_baseline(p, seed, k, budget_s):

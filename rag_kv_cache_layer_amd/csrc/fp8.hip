@@ -38,28 +38,48 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return (E - 1) - 8 + (m > 1.75f ? 1 : 0);
 }
 
+// one workgroup per row; with vec (rows a multiple of 16 elements, 16-byte
+// aligned buffers) each thread takes 16 consecutive elements per pass (16-byte
+// loads, one 16-byte store of codes), otherwise element by element
 template <typename T>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, int cols,
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x, int cols, bool vec,
                                                             uint8_t* __restrict__ q, int* __restrict__ ex) {
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   const T* xr = x + (int64_t)row * cols;
+  uint8_t* qr = q + (int64_t)row * cols;
+  const int vec_end = vec ? cols : 0;
   float amax = 0.f;
-  for (int c = tid; c < cols; c += 256) amax = fmaxf(amax, fabsf(Elem<T>::ld(xr + c)));
+  for (int c = tid * 16; c < vec_end; c += 256 * 16) {
+    float v[16];
+    load8(xr + c, v);
+    load8(xr + c + 8, v + 8);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  }
+  for (int c = vec_end + tid; c < cols; c += 256) amax = fmaxf(amax, fabsf(Elem<T>::ld(xr + c)));
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int e = row_exponent(amax);
   if (tid == 0) ex[row] = e;
-  uint8_t* qr = q + (int64_t)row * cols;
-  for (int c = 2 * tid; c < cols; c += 512) {
-    const float a = fminf(fmaxf(ldexpf(Elem<T>::ld(xr + c), -e), -448.f), 448.f);
-    const float b = c + 1 < cols ? fminf(fmaxf(ldexpf(Elem<T>::ld(xr + c + 1), -e), -448.f), 448.f) : 0.f;
-    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    qr[c] = (uint8_t)(pk & 0xff);
-    if (c + 1 < cols) qr[c + 1] = (uint8_t)((pk >> 8) & 0xff);
+  auto scaled = [&](float v) { return fminf(fmaxf(ldexpf(v, -e), -448.f), 448.f); };
+  for (int c = tid * 16; c < vec_end; c += 256 * 16) {
+    float v[16];
+    load8(xr + c, v);
+    load8(xr + c + 8, v + 8);
+    u32x4_t w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(v[4 * j]), scaled(v[4 * j + 1]), 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(scaled(v[4 * j + 2]), scaled(v[4 * j + 3]), pk, true);
+      w[j] = (uint32_t)pk;
+    }
+    *reinterpret_cast<u32x4_t*>(qr + c) = w;
   }
+  for (int c = vec_end + tid; c < cols; c += 256)
+    qr[c] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(scaled(Elem<T>::ld(xr + c)), 0.f, 0, false) & 0xff);
 }
 
 template <typename TO>
@@ -209,10 +229,11 @@ hipError_t launch_quantize_rows(int src_dtype, const void* x, int rows, int cols
                                 hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   LaunchScope ls("quantize_fp8", s);
+  const bool vec = cols % 16 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)q & 15) == 0;
   if (src_dtype == CB_BF16)
-    quantize_rows_kernel<bf16_t><<<rows, 256, 0, s>>>((const bf16_t*)x, cols, q, ex);
+    quantize_rows_kernel<bf16_t><<<rows, 256, 0, s>>>((const bf16_t*)x, cols, vec, q, ex);
   else
-    quantize_rows_kernel<float><<<rows, 256, 0, s>>>((const float*)x, cols, q, ex);
+    quantize_rows_kernel<float><<<rows, 256, 0, s>>>((const float*)x, cols, vec, q, ex);
   return hipGetLastError();
 }
 
