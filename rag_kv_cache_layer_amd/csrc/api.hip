@@ -219,11 +219,9 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   g.epi.ld_out = D.d;
   g.splits = gemm_splits(dt, gemm_n_tiles(dt, g.B, g.N), g.K);
   g.part = at<float>(ws, L.part);
-  cb_status st = hip_status(launch_gemm(dt, g, s));
-  if (st) return st;
-  // RMSNorm(h) -> hn
-  st = hip_status(launch_rmsnorm(dt, true, at<void>(ws, L.h), m_out, nullptr, nullptr, (const float*)w.mlp_norm,
-                                 at<void>(ws, L.hn), m_out, D.d, c.rms_eps, s));
+  // ... and RMSNorm(h) -> hn
+  cb_status st = hip_status(
+      launch_gemm_resid_norm(dt, g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s));
   if (st) return st;
   // gate/up + SwiGLU -> u
   GemmArgs gu{};

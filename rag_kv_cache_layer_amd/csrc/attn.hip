@@ -377,19 +377,22 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
 // Merge the key-split partials of one row in split order, for every head:
 // out = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s over the splits that
 // hold keys of the row.  Rows of tiles that were not split are skipped.  One
-// workgroup per (row, group of kMergeHeads heads): the per-(head, split)
-// weights go to LDS first, then each thread adds the splits of 4 consecutive
-// dims of one head with independent loads.
-constexpr int kMergeHeads = 8;
+// workgroup per (row, group of heads); HD / 4 threads per head, 4 dims each.
+// Every thread reads its head's (max, sum) pairs itself and issues its loads
+// before the workgroup learns whether the row's tile was split, so the
+// kernel is about two memory round trips deep (the partial buffers are
+// always in bounds; values read for a tile that was not split are dropped).
+template <int HD>
+constexpr int merge_heads() { return 256 / (HD / 4); }
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  extern __shared__ float coef[];   // [kMergeHeads][ns]
   __shared__ int s_pm;
+  constexpr int kTPH = HD / 4;
   const int i = blockIdx.x;
-  const int h0 = blockIdx.y * kMergeHeads;
-  const int nh = min(kMergeHeads, a.n_q - h0);
   const int tid = threadIdx.x;
+  const int head = blockIdx.y * merge_heads<HD>() + tid / kTPH;
+  const int c = (tid % kTPH) * 4;
   // the attention workgroup of this row's tile decided whether to split
   const TileInfo ti = tile_info(a, tile_of_row(a, i));
   if (tid < 64) {
@@ -403,41 +406,34 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o));
     if (tid == 0) s_pm = p;
   }
-  __syncthreads();
-  if (s_pm < a.key_split) return;   // this tile was written directly
   int p = a.qpos ? a.qpos[i] : i;
   p = p < 0 ? 0 : (p >= ti.T ? ti.T - 1 : p);
   const int ns = p / a.key_split + 1;
-  if (tid < nh) {
-    const int head = h0 + tid;
-    float m = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) m = fmaxf(m, a.ml_part[(((int64_t)sp * a.m + i) * a.n_q + head) * 2]);
-    float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  if (head < a.n_q) {
+    const int64_t stride = (int64_t)a.m * a.n_q;   // slots per split
+    const int64_t slot0 = (int64_t)i * a.n_q + head;
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int sp = 0; sp < ns; ++sp) mx = fmaxf(mx, a.ml_part[(slot0 + sp * stride) * 2]);
+#pragma unroll 8
     for (int sp = 0; sp < ns; ++sp) {
-      const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + (((int64_t)sp * a.m + i) * a.n_q + head) * 2);
-      const float wgt = exp2f(ml.x - m);
-      coef[tid * ns + sp] = wgt;
+      const int64_t slot = slot0 + sp * stride;
+      const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
+      const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + c);
+      const float wgt = exp2f(ml.x - mx);
       den += wgt * ml.y;
-    }
-    const float inv = 1.0f / den;
-    for (int sp = 0; sp < ns; ++sp) coef[tid * ns + sp] *= inv;
-  }
-  __syncthreads();
-  const int per_row = a.n_q * HD;
-  for (int c = tid * 4; c < nh * HD; c += 256 * 4) {
-    const int hl = c / HD, head = h0 + hl;
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < ns; ++sp) {
-      const int64_t slot = ((int64_t)sp * a.m + i) * a.n_q + head;
-      const float wgt = coef[hl * ns + sp];
-      const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + (c % HD));
       num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;
     }
-    bf16_t* Op = (bf16_t*)a.O + (int64_t)i * per_row + h0 * HD + c;
-    const uint32_t w0 = (uint32_t)f2bf(num.x) | ((uint32_t)f2bf(num.y) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(num.z) | ((uint32_t)f2bf(num.w) << 16);
-    *reinterpret_cast<uint2*>(Op) = make_uint2(w0, w1);
   }
+  __syncthreads();
+  if (s_pm < a.key_split || head >= a.n_q) return;   // tile written directly
+  const float inv = 1.0f / den;
+  bf16_t* Op = (bf16_t*)a.O + ((int64_t)i * a.n_q + head) * HD + c;
+  const uint32_t w0 = (uint32_t)f2bf(num.x * inv) | ((uint32_t)f2bf(num.y * inv) << 16);
+  const uint32_t w1 = (uint32_t)f2bf(num.z * inv) | ((uint32_t)f2bf(num.w * inv) << 16);
+  *reinterpret_cast<uint2*>(Op) = make_uint2(w0, w1);
 }
 
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, float scale) {
@@ -510,8 +506,8 @@ hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.key_split <= 0) return e;
   LaunchScope ls("attn_merge", s);
-  const size_t coef_bytes = (size_t)kMergeHeads * n_split * sizeof(float);
-  attn_merge_kernel<HD><<<dim3(a.m, (a.n_q + kMergeHeads - 1) / kMergeHeads), 256, coef_bytes, s>>>(a);
+  constexpr int hpb = merge_heads<HD>();
+  attn_merge_kernel<HD><<<dim3(a.m, (a.n_q + hpb - 1) / hpb), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

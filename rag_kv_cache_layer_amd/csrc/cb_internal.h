@@ -232,6 +232,10 @@ int gemm_bn(int dtype);                               // N tile width
 int gemm_splits(int dtype, int N_tiles, int K);       // split-K choice (independent of M)
 int gemm_n_tiles(int dtype, const BOperand& B, int N);
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
+// A residual projection into fp32 rows (epi.out) followed by the RMSNorm of
+// those rows into hn (the cache dtype), fused after split-K when possible.
+hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g, const float* gain, float eps, void* hn,
+                                  hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Attention of selected rows over the cache.

@@ -408,13 +408,13 @@ constexpr int LBM = 256, LBN = CB_BIG_BN, LBK = 32, LNS = CB_BIG_NSTAGE, LCLD = 
 constexpr int kLW = CB_BIG_WAVES;                    // waves per workgroup
 static_assert(LBN == 224 || LBN == 256, "large tile: 224 or 256 columns");
 static_assert(kLW == 8 || (kLW == 4 && LBN == 256), "8 waves, or 4 waves of 128x128");
-static_assert(LNS >= 2 && LNS <= 4, "ring depth");
 constexpr int kLNT = 64 * kLW;
 constexpr int kLWN = kLW == 4 ? 2 : (LBN == 224 ? 2 : 4);   // waves along N
 constexpr int kLWTM = LBM / (kLW / kLWN);            // wave tile rows (64 or 128)
 constexpr int kLWTN = LBN / kLWN;                    // wave tile columns (112, 64 or 128)
 constexpr int kLFA = kLWTM / 16, kLFB = kLWTN / 16;  // MFMA blocks per wave
 constexpr int kLStage = (LBM + LBN) * LBK * 2;       // 30 or 32 KB
+static_assert(LNS >= 2 && LNS <= 5 && LNS * kLStage <= 160 * 1024, "ring depth");
 constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LCLD * 4;
 constexpr int kLBlocksA = LBM / 16, kLBlocks = (LBM + LBN) / 16;   // 1 KB blocks per stage
 constexpr int kLBPW = (kLBlocks + kLW - 1) / kLW;   // blocks per wave (at most)
@@ -434,10 +434,12 @@ __device__ __forceinline__ int swz32(int r, int c) {
 }
 
 // s_waitcnt with the later steps' loads still allowed in flight (ps loads per
-// step, later <= 2 steps)
+// step, later <= 4 steps)
 #define CB_WAIT_LATER(ps, later)                 \
   do {                                           \
-    if ((later) >= 2) CB_WAIT_VMCNT(2 * (ps));   \
+    if ((later) >= 4) CB_WAIT_VMCNT(4 * (ps));   \
+    else if ((later) == 3) CB_WAIT_VMCNT(3 * (ps)); \
+    else if ((later) == 2) CB_WAIT_VMCNT(2 * (ps)); \
     else if ((later) == 1) CB_WAIT_VMCNT(ps);    \
     else CB_WAIT_VMCNT(0);                       \
   } while (0)
@@ -630,6 +632,61 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, int nt
   }
 }
 
+// Split-K finish of a residual projection fused with the RMSNorm that follows
+// it (attention output projection -> h -> RMSNorm -> the MLP input): one
+// 256-thread workgroup per row; every thread owns the same 8-column groups as
+// rmsnorm_kernel and adds in the same order, so h and the normalised row are
+// bit-identical to the two kernels run one after the other.
+constexpr int kResidNormGroups = 4;  // 8-column groups per thread: rows up to 256 * 8 * 4 = 8192 wide
+
+__global__ __launch_bounds__(256) void resid_norm_kernel(GemmArgs g, int ntiles, const float* __restrict__ gain,
+                                                         float eps, bf16_t* __restrict__ hn) {
+  __shared__ float red[4];
+  const int gm = blockIdx.x;
+  const int ldp = ntiles * BN;
+  const int d = g.N;
+  const EpiParams& e = g.epi;
+  const int r = map_row(gm, e.rmap1, e.rmap2);
+  float* hrow = (float*)e.out + (int64_t)gm * d;
+  float h[kResidNormGroups][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kResidNormGroups; ++i) {
+    const int c = (threadIdx.x + i * 256) * 8;
+    if (c < d) {
+      float v[8], x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      sum8<EPI_RESID>(g, ldp, gm, c, v);
+      if (r >= 0 && r < e.T) {
+        if (e.resid_f32) load8((const float*)e.resid + (int64_t)r * d + c, x);
+        else load8((const bf16_t*)e.resid + (int64_t)r * d + c, x);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h[i][j] = x[j] + v[j];  // h = residual + projection (fp32)
+        ss += h[i][j] * h[i][j];
+      }
+      store8(hrow + c, h[i]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rs = sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < kResidNormGroups; ++i) {
+    const int c = (threadIdx.x + i * 256) * 8;
+    if (c < d) {
+      float gg[8], o[8];
+      load8(gain + c, gg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = (h[i][j] / rs) * gg[j];
+      store8(hn + (int64_t)gm * d + c, o);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 SIMT kernel
 // ---------------------------------------------------------------------------
@@ -711,6 +768,29 @@ int gemm_splits(int dtype, int n_tiles, int K) {
   int s = 1;
   while (s < 4 && n_tiles * s < CB_SPLIT_TILES && K / (2 * s) >= 1024) s *= 2;
   return s;
+}
+
+hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g0, const float* gain, float eps, void* hn,
+                                  hipStream_t s) {
+  if (g0.M <= 0) return hipSuccess;
+  if (dtype != CB_BF16 || g0.splits <= 1 || g0.epi.kind != EPI_RESID || !g0.epi.out_f32 || g0.N % 8 ||
+      g0.N > 256 * 8 * kResidNormGroups || g0.epi.ld_out != g0.N) {
+    hipError_t e = launch_gemm(dtype, g0, s);
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm(dtype, true, g0.epi.out, g0.M, nullptr, nullptr, gain, hn, g0.M, g0.N, eps, s);
+  }
+  GemmArgs g = g0;
+  const int ntiles = gemm_n_tiles(dtype, g.B, g.N);
+  const int mt = (g.M + BM - 1) / BM;
+  {
+    LaunchScope ls("gemm_o", s);
+    gemm_bf16_kernel<EPI_RESID><<<dim3(mt * ntiles, g.splits), 256, 0, s>>>(g, mt, ntiles);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LaunchScope ls("resid_norm", s);
+  resid_norm_kernel<<<g.M, 256, 0, s>>>(g, ntiles, gain, eps, (bf16_t*)hn);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
