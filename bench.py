@@ -233,6 +233,7 @@ def main():
         torch.cuda.synchronize()
         extra["full_prefill_ms"] = round((time.perf_counter() - t0) * 100, 4)
         extra["shift_stack"] = shift_stack_measure()
+        extra["kv_expand_stack"] = kv_expand_measure()
 
     if args.batch > 1:
         # n_req requests of the same shape (own caches, same rows): one shift
@@ -364,6 +365,41 @@ def shift_stack_measure(reps=6):
             "copy_same_bytes_gbs": round(nbytes / (cms * 1e-3) / 1e9, 1)}
 
 
+def kv_expand_measure(reps=6):
+    """cb_kv_from_fp8 over a whole 32-layer 8B stack (8 x 512 + 64 tokens):
+    8-bit K and V codes of every row expanded into bf16 caches with the keys
+    re-aligned, one launch, alternating between two destination pairs so that
+    no call finds its data in the Infinity Cache.  Algorithmic bytes: codes
+    and exponents read once, the bf16 caches written once."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+    p = synth.PRESETS["llama8b_stack"]
+    cfg = F.config_of(p)
+    offs = synth.chunk_offsets(p, range(p.n_chunks))
+    T, kvd, L, H = p.T, p.kv_dim, p.n_layers, p.n_kv_heads
+    rope = F.DeviceRope(cfg, T)
+    codes = [torch.randint(0, 0x7E, (L, T, kvd), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    exps = [torch.randint(-12, 4, (L, T, H), dtype=torch.int32, device="cuda") for _ in range(2)]
+    dsts = [[torch.empty((L, T, kvd), dtype=torch.bfloat16, device="cuda") for _ in range(2)] for _ in range(2)]
+    run = lambda i: F.kv_from_fp8(cfg, rope, codes[0], exps[0], codes[1], exps[1], dsts[i % 2][0], dsts[i % 2][1],
+                                  T * kvd, L, T, offs)
+    run(0)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run(i + 1)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    nbytes = 2 * L * T * (kvd + H * 4) + 2 * L * T * kvd * 2
+    return {"layers": L, "rows": T, "bytes": nbytes, "ms": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def pipeline_measure(seed, reps=3):
     """The 32-layer 8B-shaped stack (8 x 512 + 64 tokens, r 0.30 -> 0.15) with
     every layer's chunk KV in pinned host memory (CacheBlend section 5): the
@@ -430,6 +466,29 @@ def pipeline_measure(seed, reps=3):
     t_load = timed(load)
     t_comp = timed(resident)    # align + recompute with the KV already in device memory
     t_pipe = timed(streamed)    # load each layer (copy stream) + align + recompute (compute stream)
+    # the same KV stored as 8-bit codes with one exponent per (token, KV head):
+    # half the bytes over the link, expanded (and re-aligned) on the device
+    q8 = []
+    for X in (K, V):
+        X.copy_(Kh if X is K else Vh)
+        c, e = F.quantize_fp8(X.view(-1, p.head_dim))
+        q8 += [c.view(shape).cpu().pin_memory(), e.view(shape[:3]).cpu().pin_memory()]
+    torch.cuda.synchronize()
+    kc8, ke8, vc8, ve8 = q8
+    d8 = [torch.empty(t.shape, dtype=t.dtype, device="cuda") for t in q8]
+    kv8_bytes = sum(t.numel() * t.element_size() for t in q8)
+
+    def load8():
+        with torch.cuda.stream(cs):
+            for d_, s_ in zip(d8, q8):
+                d_.copy_(s_, non_blocking=True)
+
+    def streamed8():
+        F.blend_stack_native(cfg, layers, rope, K, V, T, offs, x0, ks, wss, k_src=kc8, v_src=vc8,
+                             k_src_exp=ke8, v_src_exp=ve8, copy_stream=cs)
+
+    t_load8 = timed(load8)
+    t_pipe8 = timed(streamed8)
     # one full-prefill layer over the context, for the controller's recompute estimate
     h_in = torch.randn((T, p.d_model), generator=g, device="cuda").to(torch.bfloat16)
     h_out = torch.empty_like(h_in)
@@ -445,7 +504,13 @@ def pipeline_measure(seed, reps=3):
             "pipelined_ms": round(t_pipe * 1e3, 3), "link_gbs": round(link / 1e9, 2),
             "hidden_fraction": round((t_load + t_comp - t_pipe) / min(t_load, t_comp), 3),
             "pcie_inclusive_tokens_per_s": round(T / t_pipe, 1),
-            "full_prefill_layer_ms": round(t_pf * 1e3, 4), "controller_r_e4": r_e4}
+            "full_prefill_layer_ms": round(t_pf * 1e3, 4), "controller_r_e4": r_e4,
+            "kv8": {"kv_bytes": kv8_bytes, "load_ms": round(t_load8 * 1e3, 3),
+                    "pipelined_ms": round(t_pipe8 * 1e3, 3),
+                    "hidden_fraction": round((t_load8 + t_comp - t_pipe8) / min(t_load8, t_comp), 3),
+                    "pcie_inclusive_tokens_per_s": round(T / t_pipe8, 1),
+                    "controller_r_e4": F.pick_ratio(t_pf * 1e6, kv8_bytes / (p.n_layers * T), T, link * 1e-6,
+                                                    1500)}}
 
 
 def analytics_measure(seed):

@@ -138,7 +138,8 @@ size_t cb_workspace_size(const cb_layer_config* cfg, int32_t T, int32_t m_max);
 
 /* Bytes of device workspace needed by cb_blend_stack over T rows: the
  * per-layer workspace of cb_workspace_size(cfg, T, T), two [T][d] hidden
- * buffers and a [T] row list.  0 on invalid cfg or T <= 0. */
+ * buffers, a [T] row list and two staging slots for one layer's 8-bit K/V
+ * (cb_blend_stack_kv8).  0 on invalid cfg or T <= 0. */
 size_t cb_stack_workspace_size(const cb_layer_config* cfg, int32_t T);
 
 /* Loading controller of section 5: the recompute ratio of one layer, in
@@ -356,6 +357,52 @@ cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers, const cb_
                          const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all,
                          void* hidden_out, int32_t* m_rows_host, void* ws, size_t ws_bytes,
                          void* stream, void* copy_stream);
+
+/* 8-bit stored chunk KV.  The paper serves its larger models with 8-bit
+ * weights (section 7); the same E4M3 format halves the bytes of the stored
+ * KV that the loader of section 5 moves (one power-of-two exponent per
+ * (token, KV head) row of head_dim values, as cb_quantize_fp8 produces over
+ * rows of head_dim).
+ *
+ * cb_kv_from_fp8: expands codes into the caches, K and V of rows
+ * row_begin .. row_begin+n_rows-1 of n_layers layers:
+ *  k_codes, v_codes: device uint8 [n_layers][n_rows][n_kv][hd], 16-byte
+ *    aligned; k_exps, v_exps: device int32 [n_layers][n_rows][n_kv].
+ *  k_cache, v_cache: device [T][n_kv][hd] in cfg->dtype, layer l at element
+ *    offset l * layer_stride_elems.  Written: value(code) * 2^exp, exact in
+ *    fp32 and bf16; with shift != 0 the keys of rows in chunk c >= 1 are
+ *    then rotated by delta = chunk_offsets[c] exactly as cb_rope_shift does
+ *    (the same bits as expanding and then shifting).  Other rows untouched.
+ *  chunk_offsets: host [n_chunks+1] as cb_rope_shift (n_chunks <= 256).
+ *  rope: device tables covering chunk_offsets[n_chunks-1] + 1 positions
+ *    (only read, and only checked, when shift != 0).
+ *  CB_ERR_SHAPE when hd is not a multiple of 16 or rows exceed T; other
+ *  errors as cb_rope_shift. */
+cb_status cb_kv_from_fp8(const cb_layer_config* cfg, const cb_rope_dev* rope,
+                         const uint8_t* k_codes, const int32_t* k_exps,
+                         const uint8_t* v_codes, const int32_t* v_exps, int32_t n_layers,
+                         int32_t row_begin, int32_t n_rows, void* k_cache, void* v_cache,
+                         int64_t layer_stride_elems, int32_t T, const int32_t* chunk_offsets,
+                         int32_t n_chunks, int32_t shift, void* stream);
+
+/* cb_blend_stack with the chunk KV of every layer loaded from 8-bit host
+ * copies: k_src, v_src host uint8 [n_layers][T][n_kv][hd] and k_src_exp,
+ * v_src_exp host int32 [n_layers][T][n_kv] (allocate with hipHostMalloc for
+ * asynchronous copies).  Layer l's codes are copied into a device staging
+ * slot in the workspace and expanded into its caches on copy_stream
+ * (cb_kv_from_fp8 over all T rows, re-aligning the keys when shift != 0);
+ * layer l's recompute waits for that expansion only.  Every other argument,
+ * the results and the errors are those of cb_blend_stack; the result equals
+ * cb_blend_stack run on caches holding the expanded values. */
+cb_status cb_blend_stack_kv8(const cb_layer_config* cfg, int32_t n_layers,
+                             const cb_layer_weights* layers, const cb_rope_dev* rope,
+                             void* k_caches, void* v_caches, int64_t layer_stride_elems,
+                             const uint8_t* k_src, const int32_t* k_src_exp,
+                             const uint8_t* v_src, const int32_t* v_src_exp, int32_t T,
+                             const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
+                             const void* x_first, const int32_t* ks, int32_t* s_out_all,
+                             float* dev_all, void* hidden_out, int32_t* m_rows_host, void* ws,
+                             size_t ws_bytes, void* stream, void* copy_stream);
 
 #ifdef __cplusplus
 }

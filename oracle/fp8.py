@@ -14,6 +14,10 @@ rounding to E4M3 loses information:
 A product C = A B^T of two such matrices is then exactly
 sum_k value(a_code) value(b_code) * 2^(e_a + e_b); every product of two
 E4M3 values is exact in fp32, so only the accumulation order rounds.
+
+Stored KV in this format (the loader of CacheBlend section 5 moves the
+chunk KV; 8 bits halve those bytes) is scaled per (token, KV head): the rows
+of the quantizer are the head_dim values of one head of one token.
 """
 from __future__ import annotations
 
@@ -91,6 +95,22 @@ def quantize_rows(x: np.ndarray):
 
 def dequantize_rows(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
     return np.ldexp(VALUES[codes], e[:, None].astype(np.int64))
+
+
+def quantize_kv(x: np.ndarray):
+    """(codes uint8 [T][n_kv][hd], exponents int32 [T][n_kv]) of a K or V
+    cache [T][n_kv][hd]: one row exponent per (token, KV head)."""
+    T, H, D = x.shape
+    c, e = quantize_rows(np.asarray(x, np.float32).reshape(T * H, D))
+    return c.reshape(T, H, D), e.reshape(T, H)
+
+
+def expand_kv(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """The fp32 cache [T][n_kv][hd] that codes and exponents stand for:
+    value(code) * 2^e, exact (an E4M3 value times a power of two is an fp32
+    and a bf16 number)."""
+    T, H, D = codes.shape
+    return dequantize_rows(codes.reshape(T * H, D), e.reshape(T * H)).astype(np.float32).reshape(T, H, D)
 
 
 def gemm(a_codes, a_e, b_codes, b_e) -> np.ndarray:

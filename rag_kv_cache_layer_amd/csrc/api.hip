@@ -103,10 +103,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Dims {
-  int d, q_dim, kv_dim, hd, F, b, bn;
+  int d, q_dim, kv_dim, n_kv, hd, F, b, bn;
   explicit Dims(const cb_layer_config& c)
-      : d(c.d_model), q_dim(c.n_q_heads * c.head_dim), kv_dim(c.n_kv_heads * c.head_dim), hd(c.head_dim),
-        F(c.ffn_dim), b(c.dtype == CB_BF16 ? 2 : 4), bn(gemm_bn(c.dtype)) {}
+      : d(c.d_model), q_dim(c.n_q_heads * c.head_dim), kv_dim(c.n_kv_heads * c.head_dim), n_kv(c.n_kv_heads),
+        hd(c.head_dim), F(c.ffn_dim), b(c.dtype == CB_BF16 ? 2 : 4), bn(gemm_bn(c.dtype)) {}
   int n_qkv() const { return q_dim + 2 * kv_dim; }
   int k_tile0() const { return q_dim / bn; }
   int n_k_tiles() const { return (q_dim + kv_dim - 1) / bn - k_tile0() + 1; }
@@ -634,10 +634,18 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
 // the fusor over a stack of layers, with KV loading pipelined with recompute
 // ---------------------------------------------------------------------------
 
+namespace {
+// staging of one layer's 8-bit K/V (codes, then exponents) on the device
+size_t kv8_slot_bytes(const Dims& D, int T) {
+  return 2 * align256((size_t)T * D.kv_dim) + 2 * align256((size_t)T * D.n_kv * 4);
+}
+}  // namespace
+
 extern "C" size_t cb_stack_workspace_size(const cb_layer_config* cfg, int32_t T) {
   if (check_cfg(cfg) != CB_OK || T <= 0) return 0;
   const Dims D(*cfg);
-  return align256(cb_workspace_size(cfg, T, T)) + 2 * align256((size_t)T * D.d * D.b) + align256((size_t)T * 4);
+  return align256(cb_workspace_size(cfg, T, T)) + 2 * align256((size_t)T * D.d * D.b) + align256((size_t)T * 4) +
+         2 * kv8_slot_bytes(D, T);
 }
 
 extern "C" int32_t cb_pick_ratio(double t_prefill_us, double kv_bytes_per_token, int32_t n_tokens,
@@ -655,19 +663,33 @@ extern "C" int32_t cb_pick_ratio(double t_prefill_us, double kv_bytes_per_token,
   return std::max(r, r_min_e4);
 }
 
-extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers, const cb_layer_weights* layers,
-                                    const cb_rope_dev* rope, void* k_caches, void* v_caches,
-                                    int64_t layer_stride_elems, const void* k_src, const void* v_src, int32_t T,
-                                    const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
-                                    const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all,
-                                    void* hidden_out, int32_t* m_rows_host, void* ws, size_t ws_bytes, void* stream,
-                                    void* copy_stream) {
+namespace {
+
+// where the chunk KV of every layer comes from: nowhere (already in the
+// device caches), host copies in the cache dtype, or host 8-bit codes with
+// per-(row, KV head) exponents
+struct KvSource {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* k_exp = nullptr;
+  const int32_t* v_exp = nullptr;
+  bool fp8 = false;
+};
+
+cb_status stack_run(const cb_layer_config* cfg, int32_t n_layers, const cb_layer_weights* layers,
+                    const cb_rope_dev* rope, void* k_caches, void* v_caches, int64_t layer_stride_elems,
+                    const KvSource& src, int32_t T, const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
+                    const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all, void* hidden_out,
+                    int32_t* m_rows_host, void* ws, size_t ws_bytes, void* stream, void* copy_stream) {
+  const void* k_src = src.k;
+  const void* v_src = src.v;
   cb_status st = check_cfg(cfg);
   if (st) return st;
   if (n_layers < 1 || !layers || !k_caches || !v_caches || !chunk_offsets || !x_first || !ks || !s_out_all ||
       !dev_all || !hidden_out || !ws || T <= 0 || n_chunks < 1)
     return CB_ERR_ARG;
   if ((k_src == nullptr) != (v_src == nullptr)) return CB_ERR_ARG;
+  if (src.fp8 && (!k_src || !src.k_exp || !src.v_exp)) return CB_ERR_ARG;
   for (int l = 0; l < n_layers; ++l) {
     st = check_weights(&layers[l]);
     if (st) return st;
@@ -688,6 +710,7 @@ extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers
   const int64_t layer_elems = (int64_t)T * D.kv_dim;
   if (n_layers > 1 && layer_stride_elems < layer_elems) return CB_ERR_SHAPE;
   if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
+  if (src.fp8 && D.hd % 16) return CB_ERR_SHAPE;
   st = check_rope(rope, T);
   if (st) return st;
   if (ws_bytes < cb_stack_workspace_size(cfg, T)) return CB_ERR_WORKSPACE;
@@ -750,15 +773,61 @@ extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers
         return st;
       }
     }
+    // 8-bit sources: two staging slots after the hidden-row buffers; layer
+    // l's codes go to slot l % 2 and are expanded (keys re-aligned) into its
+    // caches on the copy stream, which also orders the slot's reuse
+    char* stage0 = base + blend_bytes + 2 * hid_bytes + align256((size_t)T * 4);
+    const size_t code_bytes = (size_t)T * D.kv_dim, exp_bytes = (size_t)T * D.n_kv * 4;
     for (int l = 0; l < n_layers; ++l) {
       char* kd = (char*)k_caches + (int64_t)l * stride_bytes;
       char* vd = (char*)v_caches + (int64_t)l * stride_bytes;
-      const char* kh = (const char*)k_src + (int64_t)l * layer_bytes;
-      const char* vh = (const char*)v_src + (int64_t)l * layer_bytes;
-      if ((st = hip_status(hipMemcpyAsync(kd, kh, layer_bytes, hipMemcpyHostToDevice, cs))) ||
-          (st = hip_status(hipMemcpyAsync(vd, vh, layer_bytes, hipMemcpyHostToDevice, cs)))) {
-        cleanup();
-        return st;
+      if (src.fp8) {
+        char* slot = stage0 + (l & 1) * kv8_slot_bytes(D, T);
+        uint8_t* kc8 = (uint8_t*)slot;
+        uint8_t* vc8 = (uint8_t*)(slot + align256(code_bytes));
+        int32_t* ke = (int32_t*)(slot + 2 * align256(code_bytes));
+        int32_t* ve = (int32_t*)(slot + 2 * align256(code_bytes) + align256(exp_bytes));
+        const char* kh = (const char*)k_src + (int64_t)l * code_bytes;
+        const char* vh = (const char*)v_src + (int64_t)l * code_bytes;
+        const int32_t* keh = src.k_exp + (int64_t)l * T * D.n_kv;
+        const int32_t* veh = src.v_exp + (int64_t)l * T * D.n_kv;
+        if ((st = hip_status(hipMemcpyAsync(kc8, kh, code_bytes, hipMemcpyHostToDevice, cs))) ||
+            (st = hip_status(hipMemcpyAsync(vc8, vh, code_bytes, hipMemcpyHostToDevice, cs))) ||
+            (st = hip_status(hipMemcpyAsync(ke, keh, exp_bytes, hipMemcpyHostToDevice, cs))) ||
+            (st = hip_status(hipMemcpyAsync(ve, veh, exp_bytes, hipMemcpyHostToDevice, cs)))) {
+          cleanup();
+          return st;
+        }
+        KvExpandArgs xa{};
+        xa.k_codes = kc8;
+        xa.v_codes = vc8;
+        xa.k_exps = ke;
+        xa.v_exps = ve;
+        xa.k_cache = kd;
+        xa.v_cache = vd;
+        xa.layer_stride = layer_stride_elems;
+        xa.n_layers = 1;
+        xa.row0 = 0;
+        xa.n_rows = T;
+        xa.kv_dim = D.kv_dim;
+        xa.n_kv = D.n_kv;
+        xa.hd = D.hd;
+        xa.cos = rope->cos;
+        xa.sin = rope->sin;
+        xa.n_chunks = n_chunks;
+        xa.shift = shift;
+        if ((st = hip_status(launch_kv_expand(cfg->dtype, xa, chunk_offsets, cs)))) {
+          cleanup();
+          return st;
+        }
+      } else {
+        const char* kh = (const char*)k_src + (int64_t)l * layer_bytes;
+        const char* vh = (const char*)v_src + (int64_t)l * layer_bytes;
+        if ((st = hip_status(hipMemcpyAsync(kd, kh, layer_bytes, hipMemcpyHostToDevice, cs))) ||
+            (st = hip_status(hipMemcpyAsync(vd, vh, layer_bytes, hipMemcpyHostToDevice, cs)))) {
+          cleanup();
+          return st;
+        }
       }
       if (pipelined) {
         hipEvent_t e = nullptr;
@@ -789,7 +858,7 @@ extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers
         cleanup();
         return st;
       }
-      if (shift) {
+      if (shift && !src.fp8) {
         ra.k_cache = kc;
         ra.n_layers = 1;
         if ((st = hip_status(launch_rope_shift(cfg->dtype, ra, s)))) {
@@ -813,6 +882,88 @@ extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers
   }
   cleanup();
   return CB_OK;
+}
+
+}  // namespace
+
+extern "C" cb_status cb_blend_stack(const cb_layer_config* cfg, int32_t n_layers, const cb_layer_weights* layers,
+                                    const cb_rope_dev* rope, void* k_caches, void* v_caches,
+                                    int64_t layer_stride_elems, const void* k_src, const void* v_src, int32_t T,
+                                    const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
+                                    const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all,
+                                    void* hidden_out, int32_t* m_rows_host, void* ws, size_t ws_bytes, void* stream,
+                                    void* copy_stream) {
+  KvSource src;
+  src.k = k_src;
+  src.v = v_src;
+  return stack_run(cfg, n_layers, layers, rope, k_caches, v_caches, layer_stride_elems, src, T, chunk_offsets,
+                   n_chunks, shift, x_first, ks, s_out_all, dev_all, hidden_out, m_rows_host, ws, ws_bytes, stream,
+                   copy_stream);
+}
+
+extern "C" cb_status cb_blend_stack_kv8(const cb_layer_config* cfg, int32_t n_layers, const cb_layer_weights* layers,
+                                        const cb_rope_dev* rope, void* k_caches, void* v_caches,
+                                        int64_t layer_stride_elems, const uint8_t* k_src, const int32_t* k_src_exp,
+                                        const uint8_t* v_src, const int32_t* v_src_exp, int32_t T,
+                                        const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift,
+                                        const void* x_first, const int32_t* ks, int32_t* s_out_all, float* dev_all,
+                                        void* hidden_out, int32_t* m_rows_host, void* ws, size_t ws_bytes,
+                                        void* stream, void* copy_stream) {
+  if (!k_src || !v_src || !k_src_exp || !v_src_exp) return CB_ERR_ARG;
+  KvSource src;
+  src.k = k_src;
+  src.v = v_src;
+  src.k_exp = k_src_exp;
+  src.v_exp = v_src_exp;
+  src.fp8 = true;
+  return stack_run(cfg, n_layers, layers, rope, k_caches, v_caches, layer_stride_elems, src, T, chunk_offsets,
+                   n_chunks, shift, x_first, ks, s_out_all, dev_all, hidden_out, m_rows_host, ws, ws_bytes, stream,
+                   copy_stream);
+}
+
+extern "C" cb_status cb_kv_from_fp8(const cb_layer_config* cfg, const cb_rope_dev* rope, const uint8_t* k_codes,
+                                    const int32_t* k_exps, const uint8_t* v_codes, const int32_t* v_exps,
+                                    int32_t n_layers, int32_t row_begin, int32_t n_rows, void* k_cache,
+                                    void* v_cache, int64_t layer_stride_elems, int32_t T,
+                                    const int32_t* chunk_offsets, int32_t n_chunks, int32_t shift, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!k_codes || !k_exps || !v_codes || !v_exps || !k_cache || !v_cache || !chunk_offsets || n_layers < 0 ||
+      row_begin < 0 || n_rows < 0 || T < 0 || n_chunks < 1)
+    return CB_ERR_ARG;
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_cache) || !aligned16(v_cache)) return CB_ERR_ARG;
+  if (n_chunks > kMaxShiftChunks) return CB_ERR_UNSUPPORTED;
+  if (chunk_offsets[0] != 0) return CB_ERR_SHAPE;
+  for (int c = 0; c < n_chunks; ++c)
+    if (chunk_offsets[c + 1] < chunk_offsets[c]) return CB_ERR_SHAPE;
+  if (chunk_offsets[n_chunks] > T || (int64_t)row_begin + n_rows > T) return CB_ERR_SHAPE;
+  const Dims D(*cfg);
+  if (D.hd % 16) return CB_ERR_SHAPE;
+  if (n_layers > 1 && layer_stride_elems < (int64_t)T * D.kv_dim) return CB_ERR_SHAPE;
+  if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
+  if (shift) {
+    st = check_rope(rope, n_chunks > 1 ? chunk_offsets[n_chunks - 1] + 1 : 0);
+    if (st) return st;
+  }
+  KvExpandArgs a{};
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_exps = k_exps;
+  a.v_exps = v_exps;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.layer_stride = layer_stride_elems;
+  a.n_layers = n_layers;
+  a.row0 = row_begin;
+  a.n_rows = n_rows;
+  a.kv_dim = D.kv_dim;
+  a.n_kv = D.n_kv;
+  a.hd = D.hd;
+  a.cos = shift ? rope->cos : nullptr;
+  a.sin = shift ? rope->sin : nullptr;
+  a.n_chunks = n_chunks;
+  a.shift = shift;
+  return hip_status(launch_kv_expand(cfg->dtype, a, chunk_offsets, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -140,6 +140,28 @@ struct RopeShiftArgs {
 };
 hipError_t launch_rope_shift(int dtype, const RopeShiftArgs& a, hipStream_t s);
 
+// Expansion of 8-bit stored K/V (E4M3 codes, one power-of-two exponent per
+// (row, KV head)) into the cache, keys re-aligned when shift != 0.
+constexpr int kMaxShiftChunks = 256;
+struct KvExpandArgs {
+  const uint8_t* k_codes;   // [n_layers][n_rows][kv_dim]
+  const int32_t* k_exps;    // [n_layers][n_rows][n_kv]
+  const uint8_t* v_codes;
+  const int32_t* v_exps;
+  void* k_cache;            // layer l, row r at l * layer_stride + r * kv_dim
+  void* v_cache;
+  int64_t layer_stride;
+  int n_layers;
+  int row0;                 // first cache row written
+  int n_rows;
+  int kv_dim, n_kv, hd;     // hd a multiple of 16
+  const float* cos;         // RoPE tables (when shift)
+  const float* sin;
+  int n_chunks;
+  int shift;
+};
+hipError_t launch_kv_expand(int dtype, const KvExpandArgs& a, const int32_t* offsets, hipStream_t s);
+
 // RMSNorm of gathered rows: out[i] = x[map(i)] / sqrt(mean(x^2) + eps) * g.
 // x_f32 selects an fp32 input regardless of the storage dtype.
 // out[i] = start + i for i < n (the row list of a stack's first layer)

@@ -97,6 +97,9 @@ def lib() -> ctypes.CDLL:
         "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
         "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
                                  P, P]),
+        "cb_blend_stack_kv8": (I32, [CFG, I32, W, R, P, P, I64, P, P, P, P, I32, I32P, I32, I32, P, I32P, P, P, P,
+                                     I32P, P, SZ, P, P]),
+        "cb_kv_from_fp8": (I32, [CFG, R, P, P, P, P, I32, I32, I32, P, P, I64, I32, I32P, I32, I32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -413,12 +416,14 @@ def stack_rows(T: int, chunk_offsets: Sequence[int], ks: Sequence[int]):
 
 def blend_stack_native(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: DeviceRope, k_caches, v_caches,
                        T: int, chunk_offsets: Sequence[int], x_first, ks: Sequence[int], ws, k_src=None, v_src=None,
-                       shift: bool = True, stream=None, copy_stream=None):
+                       shift: bool = True, stream=None, copy_stream=None, k_src_exp=None, v_src_exp=None):
     """cb_blend_stack: the whole stack in one library call.
 
     k_caches, v_caches: device [n_layers][T][n_kv][hd].  k_src, v_src: None,
     or host tensors of the same shape (pinned for overlap) whose copies run on
-    copy_stream (a torch stream; None = on `stream`).  ws: uint8 device
+    copy_stream (a torch stream; None = on `stream`).  With k_src_exp and
+    v_src_exp (host int32 [n_layers][T][n_kv]) the sources are 8-bit E4M3
+    codes (uint8) and cb_blend_stack_kv8 runs instead.  ws: uint8 device
     tensor of stack_workspace_size bytes.  Returns a list of per-layer dicts
     (dev, s_out as views into the concatenated outputs; y only for the last
     layer), like blend_stack."""
@@ -437,25 +442,35 @@ def blend_stack_native(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: De
     y = torch.empty((max(m_out[-1], 1), d), dtype=dt, device=dev_)
     W = (LayerWeights * n)(*[l.struct for l in layers])
     rows = (ctypes.c_int32 * (2 * n))()
-    if (k_src is None) != (v_src is None):
-        raise ValueError("k_src and v_src go together")
+    if (k_src is None) != (v_src is None) or (k_src_exp is None) != (v_src_exp is None):
+        raise ValueError("k_src and v_src (and their exponents) go together")
+    q8 = k_src_exp is not None
+    if q8 and k_src is None:
+        raise ValueError("exponents without 8-bit sources")
     src = []
-    for name, t in (("k_src", k_src), ("v_src", v_src)):
+    for name, t, want, numel in (("k_src", k_src, torch.uint8 if q8 else dt, n * T * kv),
+                                 ("v_src", v_src, torch.uint8 if q8 else dt, n * T * kv),
+                                 ("k_src_exp", k_src_exp, torch.int32, n * T * cfg.n_kv_heads),
+                                 ("v_src_exp", v_src_exp, torch.int32, n * T * cfg.n_kv_heads)):
         if t is None:
             src.append(None)
             continue
-        if t.is_cuda or not t.is_contiguous() or t.dtype != dt or t.numel() < n * T * kv:
-            raise ValueError(f"{name} must be a contiguous host tensor of {n * T * kv} {dt} elements")
+        if t.is_cuda or not t.is_contiguous() or t.dtype != want or t.numel() < numel:
+            raise ValueError(f"{name} must be a contiguous host tensor of {numel} {want} elements")
         src.append(ctypes.c_void_p(t.data_ptr()))
     cs = None if copy_stream is None else ctypes.c_void_p(copy_stream.cuda_stream)
     L0 = int(offs[1]) if len(offs) > 2 else int(offs[-1])
-    _check(lib().cb_blend_stack(ctypes.byref(cfg), n, W, ctypes.byref(rope.struct),
-                                _dptr(k_caches, "k_caches", dt, n * T * kv), _dptr(v_caches, "v_caches", dt, n * T * kv),
-                                T * kv, src[0], src[1], T, offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                                len(offs) - 1, 1 if shift else 0, _dptr(x_first, "x_first", dt, (T - L0) * d),
-                                ks_a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _dptr(s_all, "s_out_all"),
-                                _dptr(dev_all, "dev_all"), _dptr(y, "hidden_out"), rows,
-                                _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), cs), "cb_blend_stack")
+    common_head = (ctypes.byref(cfg), n, W, ctypes.byref(rope.struct), _dptr(k_caches, "k_caches", dt, n * T * kv),
+                   _dptr(v_caches, "v_caches", dt, n * T * kv), T * kv)
+    common_tail = (T, offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(offs) - 1, 1 if shift else 0,
+                   _dptr(x_first, "x_first", dt, (T - L0) * d), ks_a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                   _dptr(s_all, "s_out_all"), _dptr(dev_all, "dev_all"), _dptr(y, "hidden_out"), rows,
+                   _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream), cs)
+    if q8:
+        _check(lib().cb_blend_stack_kv8(*common_head, src[0], src[2], src[1], src[3], *common_tail),
+               "cb_blend_stack_kv8")
+    else:
+        _check(lib().cb_blend_stack(*common_head, src[0], src[1], *common_tail), "cb_blend_stack")
     out, oi, oo = [], 0, 0
     for l in range(n):
         out.append({"dev": dev_all[oi:oi + m_in[l]], "s_out": s_all[oo:oo + m_out[l]]})
@@ -468,6 +483,27 @@ def blend_stack_native(cfg: LayerConfig, layers: Sequence[DeviceLayer], rope: De
 # ---------------------------------------------------------------------------
 # fp8 E4M3 operands
 # ---------------------------------------------------------------------------
+
+def kv_from_fp8(cfg: LayerConfig, rope: Optional[DeviceRope], k_codes, k_exps, v_codes, v_exps, k_cache, v_cache,
+                layer_stride: int, n_layers: int, T: int, chunk_offsets: Sequence[int], row_begin: int = 0,
+                n_rows: Optional[int] = None, shift: bool = True, stream=None):
+    """cb_kv_from_fp8: expand 8-bit K/V codes (device uint8 [n_layers][n_rows][n_kv][hd],
+    exponents int32 [n_layers][n_rows][n_kv]) into rows row_begin.. of the caches."""
+    torch = _torch()
+    dt = torch_dtype(cfg)
+    kv = cfg.n_kv_heads * cfg.head_dim
+    n_rows = T - row_begin if n_rows is None else n_rows
+    offs = np.ascontiguousarray(np.asarray(chunk_offsets, dtype=np.int32))
+    need = (n_layers - 1) * layer_stride + T * kv if n_layers > 0 else 0
+    nc, ne = n_layers * n_rows * kv, n_layers * n_rows * cfg.n_kv_heads
+    _check(lib().cb_kv_from_fp8(ctypes.byref(cfg), ctypes.byref(rope.struct) if rope is not None else None,
+                                _dptr(k_codes, "k_codes", torch.uint8, nc), _dptr(k_exps, "k_exps", torch.int32, ne),
+                                _dptr(v_codes, "v_codes", torch.uint8, nc), _dptr(v_exps, "v_exps", torch.int32, ne),
+                                n_layers, row_begin, n_rows, _dptr(k_cache, "k_cache", dt, need),
+                                _dptr(v_cache, "v_cache", dt, need), layer_stride, T,
+                                offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(offs) - 1,
+                                1 if shift else 0, _stream(stream)), "cb_kv_from_fp8")
+
 
 def quantize_fp8(x, codes=None, exps=None, stream=None):
     """cb_quantize_fp8 of a device matrix x [rows][cols] (bf16 or fp32);

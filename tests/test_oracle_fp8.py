@@ -11,7 +11,12 @@
   random rows and for the edge cases amax = 448 * 2^k (exact fit) and just
   above; an all-zero row gets 0.
 * The GEMM of quantized operands equals the brute-force sum of products of
-  the decoded values."""
+  the decoded values.
+* Stored KV: a cache already on the scaled E4M3 grid survives quantize ->
+  expand bit for bit (expansion is exact), each (token, head) row gets its
+  own exponent, hand-built codes decode to their values, and any cache comes
+  back within half a quantum of its row's binade; the expanded values are
+  bf16 numbers."""
 import numpy as np
 import pytest
 
@@ -73,3 +78,32 @@ def test_quantized_gemm_is_the_sum_of_decoded_products():
             assert c[i, j] == pytest.approx(s, rel=1e-12, abs=1e-15)
     # the quantization error is within half a quantum of each value's binade
     assert np.max(np.abs(fp8.dequantize_rows(qa, ea) - a) / np.abs(a).max(1, keepdims=True)) <= 2.0 ** -4
+
+
+def test_kv_expand_exact_and_per_head_scale():
+    rng = np.random.default_rng(3)
+    T, H, D = 9, 3, 16
+    # values already on the grid, each (token, head) row with its own scale
+    codes = rng.integers(0, 0x7E, size=(T, H, D)).astype(np.uint8) | (rng.integers(0, 2, (T, H, D)) << 7).astype(np.uint8)
+    codes[..., 0] = 0x7E                                   # every row reaches 448: exponent = the row's scale
+    e = rng.integers(-20, 20, size=(T, H)).astype(np.int32)
+    x = (fp8.VALUES[codes] * 2.0 ** e[..., None]).astype(np.float32)
+    c2, e2 = fp8.quantize_kv(x)
+    assert np.array_equal(e2, e)
+    assert np.array_equal(fp8.VALUES[c2], fp8.VALUES[codes])
+    back = fp8.expand_kv(c2, e2)
+    assert back.dtype == np.float32 and np.array_equal(back, x)
+    # hand-built codes: 0x38 = 1, 0x01 = 2^-9, 0xC0 = -2 at the row scales below
+    hc = np.zeros((1, 2, 16), np.uint8)
+    hc[0, 0, :3] = [0x38, 0x01, 0xC0]
+    hc[0, 1, :3] = [0x38, 0x01, 0xC0]
+    he = np.array([[0, 5]], np.int32)
+    v = fp8.expand_kv(hc, he)
+    assert list(v[0, 0, :3]) == [1.0, 2.0 ** -9, -2.0] and list(v[0, 1, :3]) == [32.0, 2.0 ** -4, -64.0]
+    # any cache: within half a quantum of the row's binade; bf16-representable
+    y = (rng.normal(size=(T, H, D)) * np.exp(rng.uniform(-8, 8, (T, H, 1)))).astype(np.float32)
+    cy, ey = fp8.quantize_kv(y)
+    z = fp8.expand_kv(cy, ey)
+    assert np.all(np.abs(z - y) <= 2.0 ** -4 * np.abs(y).max(2, keepdims=True))
+    u = z.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
