@@ -587,9 +587,9 @@ def fp8_measure(p, m, steps):
             call()
         st = F.profile_end()
         torch.cuda.synchronize()
-        gm = st["gemm_fp8"]["total_ms"] / st["gemm_fp8"]["launches"]
-        if "gemm_fp8_split_sum" in st:
-            gm += st["gemm_fp8_split_sum"]["total_ms"] / st["gemm_fp8_split_sum"]["launches"]
+        # 128x128 kernel (+ split-K sum) or the 256x256 kernel for wide outputs
+        gm = sum(st[k]["total_ms"] / st[k]["launches"] for k in ("gemm_fp8", "gemm_fp8_big", "gemm_fp8_split_sum")
+                 if k in st)
         qm = st["quantize_fp8"]["total_ms"] / st["quantize_fp8"]["launches"]
         tf = 2 * m * N * K / (gm * 1e-3) / 1e12
         out[name] = {"gemm_ms": round(gm, 5), "quantize_ms": round(qm, 5), "tflops": round(tf, 1),

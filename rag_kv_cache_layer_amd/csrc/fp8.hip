@@ -206,6 +206,136 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt,
   }
 }
 
+// gemm_fp8_big_kernel: the same product on 256x256 tiles for wide outputs
+// (enough tiles to fill the chip without split-K).  8 waves of 128x64, K
+// steps of 128 bytes, a two-stage LDS ring of 64 KB stages filled by
+// direct-to-LDS loads (the 128-byte row swizzle of the 128x128 kernel), with
+// the next stage's loads issued one 1 KB block per MFMA row.  A 256x256 tile
+// moves half the bytes per flop of a 128x128 one, which is what limits these
+// kernels.
+constexpr int QLM = 256, QLN = 256, QLNS = 2, QLCLD = QLN + 4;
+constexpr int kQLStage = (QLM + QLN) * QBK;                                   // 64 KB
+constexpr int kQLSmem = QLNS * kQLStage > 128 * QLCLD * 4 ? QLNS * kQLStage : 128 * QLCLD * 4;
+constexpr int kQLBlocksA = QLM / 8;                                           // 1 KB blocks of A per stage
+
+template <typename TO>
+__global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int mt, int ntiles) {
+  __shared__ __attribute__((aligned(16))) char smem[kQLSmem];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = (gridDim.x & 7) == 0 ? ((int)blockIdx.x & 7) * (gridDim.x >> 3) + ((int)blockIdx.x >> 3)
+                                      : (int)blockIdx.x;
+  const int tm = id % mt, tn = id / mt;
+  const int m0 = tm * QLM, n0 = tn * QLN;
+  const int M = g.M, N = g.N, K = g.K;
+  const int nk = (K + QBK - 1) / QBK;
+
+  // DMA plan: block b of a stage holds tile rows 8b .. 8b+7 (A's 256 rows,
+  // then B's); wave w fills blocks w + 8j; lane i fills slot i % 8 of row
+  // i / 8 with the logical chunk slot ^ ((row >> 1) & 7)
+  const uint32_t kOOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.B, (uint32_t)((int64_t)N * K));
+  uint32_t off[8];
+  int lcol[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int blk = w + 8 * j;
+    const bool is_a = blk < kQLBlocksA;
+    const int row = (is_a ? blk : blk - kQLBlocksA) * 8 + (lane >> 3);
+    lcol[j] = ((lane & 7) ^ ((row >> 1) & 7)) * 16;
+    const int grow = (is_a ? m0 : n0) + row;
+    off[j] = grow < (is_a ? M : N) ? (uint32_t)((int64_t)grow * K) : kOOB;
+  }
+  auto issue_group = [&](int stage, int k0, int j) {
+    const int blk = w + 8 * j;
+    const int kk = k0 + lcol[j];
+    const uint32_t o = (kk < K && off[j] != kOOB) ? off[j] + kk : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(blk < kQLBlocksA ? ra : rb,
+                                             (lds_void*)(smem + stage * kQLStage + blk * 1024), 16, o, 0, 0, 0);
+  };
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wm = (w >> 2) * 128, wn = (w & 3) * 64;
+  const int fr = lane & 15, fc = lane >> 4;
+  auto frag = [&](const char* base, int r) {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + qswz(r, 2 * fc));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + qswz(r, 2 * fc + 1));
+    return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+#pragma unroll
+  for (int j = 0; j < 8; ++j) issue_group(0, 0, j);
+  for (int it = 0; it < nk; ++it) {
+    CB_WAIT_VMCNT(0);   // this wave's blocks of step it landed (nothing later is in flight)
+    CB_BARRIER();       // every wave's, and every wave is done reading the other stage
+    const int stage = it & 1;
+    const bool more = it + 1 < nk;
+    const char* sa = smem + stage * kQLStage;
+    const char* sb = sa + QLM * QBK;
+    i32x8_t af[8], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = frag(sa, wm + i * 16 + fr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[j] = frag(sb, wn + j * 16 + fr);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0,
+                                                                      127);
+      if (more) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_group(stage ^ 1, (it + 1) * QBK, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  CB_WAIT_VMCNT(0);
+  __syncthreads();
+
+  // scale by 2^(e_a + e_b) (exact); write through an fp32 tile of 128 rows
+  float* Cs = (float*)smem;
+  const bool vec = (g.ldc & 7) == 0 && ((uintptr_t)g.C & 15) == 0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((wm >> 7) == half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wn + j * 16 + fr;
+          const int eb = col < N ? g.b_exp[col] : 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int rr = i * 16 + fc * 4 + v;   // row within the half
+            const int row = m0 + half * 128 + rr;
+            const int ea = row < M ? g.a_exp[row] : 0;
+            Cs[rr * QLCLD + wn + j * 16 + fr] = ldexpf(acc[i][j][v], ea + eb);
+          }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 128 * (QLN / 8); idx += 512) {
+      const int r = idx / (QLN / 8), c = (idx % (QLN / 8)) * 8;
+      const int row = m0 + half * 128 + r, col = n0 + c;
+      if (row >= M) continue;
+      TO* dst = (TO*)g.C + (int64_t)row * g.ldc + col;
+      const float* src = Cs + r * QLCLD + c;
+      if (vec && col + 8 <= N) {
+        store8(dst, src);
+      } else {
+        for (int x = 0; x < 8 && col + x < N; ++x) Elem<TO>::st(dst + x, src[x]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename TO>
 __global__ __launch_bounds__(256) void fp8_split_sum_kernel(Fp8GemmArgs g) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -239,6 +369,17 @@ hipError_t launch_quantize_rows(int src_dtype, const void* x, int rows, int cols
 
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& g, int out_dtype, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  {
+    // wide outputs: 256x256 tiles when they alone give ~3/4 of a wave of
+    // workgroups per CU (the 128x128 kernel would not split K either)
+    const int lmt = (g.M + QLM - 1) / QLM, lnt = (g.N + QLN - 1) / QLN;
+    if (g.splits == 1 && lmt * lnt >= 192) {
+      LaunchScope ls("gemm_fp8_big", s);
+      if (out_dtype == CB_BF16) gemm_fp8_big_kernel<bf16_t><<<lmt * lnt, 512, 0, s>>>(g, lmt, lnt);
+      else gemm_fp8_big_kernel<float><<<lmt * lnt, 512, 0, s>>>(g, lmt, lnt);
+      return hipGetLastError();
+    }
+  }
   const int mt = (g.M + QBM - 1) / QBM, nt = (g.N + QBN - 1) / QBN;
   const dim3 grid(mt * nt, g.splits);
   {

@@ -7,9 +7,10 @@ against the oracle (oracle/fp8.py).
   that fall below the smallest subnormal, ties).  The rounding decision is an
   integer result taken in the same precision on both sides.
 * GEMM: fp32 output within 1e-4 of the oracle's fp64 sum of the decoded
-  products (per tensor, max |x - y| / max |y|), ragged tiles, the split-K path
-  and the 8B layer's projection shapes (rows sampled); bf16 output within
-  bf16 rounding.  Every product of two E4M3 values is exact, but the matrix
+  products (per tensor, max |x - y| / max |y|), ragged tiles, the split-K path,
+  the 256x256 kernel for wide outputs (ragged rows, columns and K; vector and
+  element stores) and the 8B layer's projection shapes (rows sampled); bf16
+  output within bf16 rounding.  Every product of two E4M3 values is exact, but the matrix
   core adds the products of a 128-long block at a precision below fp32 (the
   measured difference from an exact sum is about 1e-5 of the largest
   output), hence 1e-4 rather than fp32 rounding; it is still 500x below the
@@ -59,7 +60,8 @@ def test_quantize_bit_exact(src, shape):
     assert np.array_equal(fold(got), fold(wc))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 200, 528), (130, 257, 4096), (200, 128, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 200, 528), (130, 257, 4096), (200, 128, 1024),
+                                   (300, 24584, 528), (257, 24653, 400)])
 def test_gemm_matches_oracle(M, N, K):
     need_gpu()
     rng = np.random.default_rng(M + N + K)
