@@ -285,6 +285,34 @@ def main():
         extra["analytics"] = analytics_measure(seed)
     if args.fp8:
         extra["fp8"] = fp8_measure(p, m, args.steps)
+        # the same step with the layer's projections in 8 bits (cb_blend_layer_fp8)
+        layer8 = F.DeviceLayerFp8.quantized(cfg, layer)
+        ws8 = F.workspace_fp8(cfg, T, T, dev)
+        kb8, vb8 = k_pre.clone(), v_pre.clone()
+
+        def step8():
+            F.rope_shift(cfg, rope, kb8, T * kvd, 1, T, offs)
+            F.blend_layer_fp8(cfg, layer8, rope, kb8, vb8, T, n_ctx, L0, S, m, h_full, S, k, hout, dv, s_out, ws8)
+
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step8()
+        torch.cuda.synchronize()
+        ms8 = (time.perf_counter() - t0) * 1e3 / args.steps
+        F.profile_begin()
+        for _ in range(args.steps):
+            step8()
+        st8 = F.profile_end()
+        torch.cuda.synchronize()
+        extra["fp8"]["layer"] = {
+            "ms_per_step": round(ms8, 5), "tokens_per_s": round(T / (ms8 * 1e-3), 1),
+            "speedup_vs_bf16": round(ms / ms8, 3),
+            "kernels": {n: {"avg_ms": round(v["total_ms"] / v["launches"], 5),
+                            "launches_per_step": v["launches"] // args.steps} for n, v in st8.items()}}
+        del layer8, ws8, kb8, vb8
 
     cpu = None
     log(f"gpu timing done: {ms:.4f} ms/step")

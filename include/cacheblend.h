@@ -385,6 +385,46 @@ cb_status cb_kv_from_fp8(const cb_layer_config* cfg, const cb_rope_dev* rope,
                          int64_t layer_stride_elems, int32_t T, const int32_t* chunk_offsets,
                          int32_t n_chunks, int32_t shift, void* stream);
 
+/* One layer's weights as 8-bit E4M3 codes with one power-of-two exponent
+ * per output row (cb_quantize_fp8 over the rows of each [out][in] matrix):
+ *  w_qkv [q_dim + 2 kv_dim][d]: the rows of W_q, then W_k, then W_v;
+ *  w_o [d][q_dim]; w_gu [2 ffn][d]: the rows of W_gate, then W_up;
+ *  w_down [d][ffn]; e_* int32 [rows]; attn_norm, mlp_norm fp32 [d].
+ * Device pointers, codes 16-byte aligned. */
+typedef struct {
+  const float* attn_norm;
+  const uint8_t* w_qkv;
+  const int32_t* e_qkv;
+  const uint8_t* w_o;
+  const int32_t* e_o;
+  const float* mlp_norm;
+  const uint8_t* w_gu;
+  const int32_t* e_gu;
+  const uint8_t* w_down;
+  const int32_t* e_down;
+} cb_layer_weights_fp8;
+
+/* Bytes of workspace cb_blend_layer_fp8 needs (cb_workspace_size plus the
+ * activation codes and the fp32 products).  0 on invalid cfg. */
+size_t cb_workspace_size_fp8(const cb_layer_config* cfg, int32_t T, int32_t m_max);
+
+/* cb_blend_layer with 8-bit projections, the way the paper serves its larger
+ * models (section 7, 8-bit weights): every projection's input rows (the normalised x, the
+ * attention output, the normalised h, u; stored in bf16 as in cb_blend_layer) are quantized
+ * per row to E4M3 (as cb_quantize_fp8) and multiplied with the 8-bit weights
+ * on the fp8 matrix cores (as cb_gemm_fp8, fp32 products); RoPE, the K
+ * deviation, the scatter, the top-k, the attention, the residuals, the
+ * RMSNorms and SwiGLU are those of cb_blend_layer.  cfg->dtype must be
+ * CB_BF16 (CB_ERR_UNSUPPORTED) and d_model, q_dim and ffn_dim multiples of
+ * 16 (CB_ERR_SHAPE).  Arguments, results and other errors as cb_blend_layer;
+ * workspace >= cb_workspace_size_fp8(cfg, T, m_in). */
+cb_status cb_blend_layer_fp8(const cb_layer_config* cfg, const cb_layer_weights_fp8* w,
+                             const cb_rope_dev* rope, void* k_cache, void* v_cache, int32_t T,
+                             int32_t n_ctx, int32_t first_chunk_len, const int32_t* s_in,
+                             int32_t m_in, const void* hidden_in, const int32_t* in_rows,
+                             int32_t k_out, void* hidden_out, float* dev_out, int32_t* s_out,
+                             int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream);
+
 /* cb_blend_stack with the chunk KV of every layer loaded from 8-bit host
  * copies: k_src, v_src host uint8 [n_layers][T][n_kv][hd] and k_src_exp,
  * v_src_exp host int32 [n_layers][T][n_kv] (allocate with hipHostMalloc for

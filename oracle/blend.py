@@ -94,7 +94,7 @@ def k_deviation(k_new: np.ndarray, k_old: np.ndarray) -> np.ndarray:
 def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.ndarray,
                 n_ctx: int, s_in: np.ndarray, x_in: np.ndarray, k_out: int,
                 rowwise: bool = False, store: Optional[str] = None,
-                keep: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                keep: Optional[np.ndarray] = None, lin=None) -> Dict[str, np.ndarray]:
     """One layer of selective recompute.
 
     k_cache, v_cache [T][n_kv][hd]: this layer's cache (keys already moved to
@@ -110,7 +110,8 @@ def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.
 
     keep: optional teacher forcing of step 4 -- ascending positions into s_in
     of the candidate rows to keep instead of the top-k by deviation (used to
-    compare another implementation on the same selection)."""
+    compare another implementation on the same selection).  lin: the
+    projections, as in oracle.layer (None = fp32 products with w)."""
     s_in = np.asarray(s_in, dtype=np.int64)
     T = k_cache.shape[0]
     if np.any(np.diff(s_in) <= 0):
@@ -118,7 +119,7 @@ def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.
     if not np.array_equal(s_in[s_in >= n_ctx], np.arange(n_ctx, T)):
         raise ValueError("s_in must hold every query row")
     # 1. Q/K/V of the selected rows only (Figure 5b: mask, then project)
-    q, k, v = qkv_rows(w, x_in, s_in, cfg, rowwise)
+    q, k, v = qkv_rows(w, x_in, s_in, cfg, rowwise, lin)
     k = round_store(k, store)
     v = round_store(v, store)
     # 2. deviation against the reused entry, before it is replaced
@@ -142,7 +143,7 @@ def blend_layer(w: Dict[str, np.ndarray], cfg, k_cache: np.ndarray, v_cache: np.
     # 5. attention of the kept rows over the blended cache, causal
     o = attention_rows(q[sel], kc.astype(q.dtype), vc.astype(q.dtype), s_out)
     # 6. rest of the layer for the kept rows
-    y = round_store(out_rows(w, x_in[sel], o, cfg, rowwise), store)
+    y = round_store(out_rows(w, x_in[sel], o, cfg, rowwise, lin), store)
     return {"k_cache": kc, "v_cache": vc, "dev": dev, "sel": sel, "s_out": s_out, "y": y}
 
 

@@ -113,6 +113,28 @@ def expand_kv(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
     return dequantize_rows(codes.reshape(T * H, D), e.reshape(T * H)).astype(np.float32).reshape(T, H, D)
 
 
+def quantize_layer(w) -> dict:
+    """8-bit weights of one layer: (codes, exponents) per projection matrix,
+    quantized row by row (one exponent per output row)."""
+    return {n: quantize_rows(w[n]) for n in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")}
+
+
+def projector(w8: dict, act_store="bf16"):
+    """Projections with 8-bit weights and activations, for oracle.layer's
+    ``lin`` hook: the input rows are first rounded to the dtype they are
+    stored in (the activations a projection reads are stored tensors), then
+    quantized per row; the product of the decoded operands is exact in fp64
+    and returned in fp32."""
+    from .storage import round_store
+    deq = {n: dequantize_rows(c, e) for n, (c, e) in w8.items()}
+
+    def lin(x, name):
+        xs = round_store(np.asarray(x, np.float32), act_store)
+        c, e = quantize_rows(xs)
+        return (dequantize_rows(c, e) @ deq[name].T).astype(np.float32)
+    return lin
+
+
 def gemm(a_codes, a_e, b_codes, b_e) -> np.ndarray:
     """C[m][n] = sum_k A[m][k] B[n][k] of the dequantized operands, in fp64."""
     return dequantize_rows(a_codes, a_e) @ dequantize_rows(b_codes, b_e).T

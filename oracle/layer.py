@@ -17,6 +17,10 @@ All arithmetic is in the dtype of the arrays given (fp32 by default).  With
 ``rowwise=True`` every projection is done one row at a time with a fixed
 shape, so a row's result depends only on its own input and on the keys it
 attends to; this is how the oracle reaches bit-exact prefix invariants.
+
+``lin``, when given, replaces every projection: lin(x, name) returns x times
+the weight called name (w_q, w_k, w_v, w_o, w_gate, w_up, w_down),
+transposed; the 8-bit projections of oracle/fp8.py plug in here.
 """
 from __future__ import annotations
 
@@ -76,38 +80,43 @@ def attention_rows(q: np.ndarray, k_all: np.ndarray, v_all: np.ndarray, last_key
     return out
 
 
-def qkv_rows(w: Dict[str, np.ndarray], x: np.ndarray, positions, cfg, rowwise: bool = False):
+def _proj(w, x, name, rowwise, lin):
+    return linear(x, w[name], rowwise) if lin is None else lin(x, name)
+
+
+def qkv_rows(w: Dict[str, np.ndarray], x: np.ndarray, positions, cfg, rowwise: bool = False, lin=None):
     """RMSNorm + Q/K/V projections + RoPE for rows at the given positions."""
     xn = rmsnorm(x, w["attn_norm"], cfg.rms_eps)
     n = x.shape[0]
-    q = linear(xn, w["w_q"], rowwise).reshape(n, cfg.n_q_heads, cfg.head_dim)
-    k = linear(xn, w["w_k"], rowwise).reshape(n, cfg.n_kv_heads, cfg.head_dim)
-    v = linear(xn, w["w_v"], rowwise).reshape(n, cfg.n_kv_heads, cfg.head_dim)
+    q = _proj(w, xn, "w_q", rowwise, lin).reshape(n, cfg.n_q_heads, cfg.head_dim)
+    k = _proj(w, xn, "w_k", rowwise, lin).reshape(n, cfg.n_kv_heads, cfg.head_dim)
+    v = _proj(w, xn, "w_v", rowwise, lin).reshape(n, cfg.n_kv_heads, cfg.head_dim)
     q = apply_rope(q, positions, cfg.rope_theta)
     k = apply_rope(k, positions, cfg.rope_theta)
     return q, k, v
 
 
-def out_rows(w: Dict[str, np.ndarray], x: np.ndarray, o: np.ndarray, cfg, rowwise: bool = False) -> np.ndarray:
+def out_rows(w: Dict[str, np.ndarray], x: np.ndarray, o: np.ndarray, cfg, rowwise: bool = False,
+             lin=None) -> np.ndarray:
     """Attention output projection, residual, RMSNorm, SwiGLU MLP, residual."""
     n = x.shape[0]
-    h = x + linear(o.reshape(n, -1), w["w_o"], rowwise)
+    h = x + _proj(w, o.reshape(n, -1), "w_o", rowwise, lin)
     hn = rmsnorm(h, w["mlp_norm"], cfg.rms_eps)
-    u = silu(linear(hn, w["w_gate"], rowwise)) * linear(hn, w["w_up"], rowwise)
-    return h + linear(u, w["w_down"], rowwise)
+    u = silu(_proj(w, hn, "w_gate", rowwise, lin)) * _proj(w, hn, "w_up", rowwise, lin)
+    return h + _proj(w, u, "w_down", rowwise, lin)
 
 
 def full_prefill(w: Dict[str, np.ndarray], x: np.ndarray, cfg, pos0: int = 0,
-                 rowwise: bool = False, store: Optional[str] = None):
+                 rowwise: bool = False, store: Optional[str] = None, lin=None):
     """The ordinary layer over all rows of x at positions pos0 .. pos0+T-1.
 
     Returns (K [T][n_kv][hd], V, y [T][d]); K and V are rounded to the
     storage dtype before attention reads them (they are the stored cache)."""
     T = x.shape[0]
     pos = np.arange(pos0, pos0 + T)
-    q, k, v = qkv_rows(w, x, pos, cfg, rowwise)
+    q, k, v = qkv_rows(w, x, pos, cfg, rowwise, lin)
     k = round_store(k, store)
     v = round_store(v, store)
     o = attention_rows(q, k, v, np.arange(T))
-    y = out_rows(w, x, o, cfg, rowwise)
+    y = out_rows(w, x, o, cfg, rowwise, lin)
     return k, v, round_store(y, store)

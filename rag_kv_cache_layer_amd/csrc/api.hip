@@ -194,11 +194,94 @@ cb_status check_weights(const cb_layer_weights* w) {
   return CB_OK;
 }
 
+// Extra workspace of the 8-bit layer, after the bf16 layout of the same size:
+// activation codes and row exponents, the fp32 product of one projection
+// (QKV, O, down; the gate/up product never leaves its kernel) and the fp8
+// GEMM's split-K partials.
+struct Fp8Ws {
+  size_t codes, exps, prod, part, total;
+};
+
+size_t fp8_part_bytes(int M, int N, int K) {
+  const int sp = fp8_splits(N, K);
+  return sp > 1 ? (size_t)sp * M * N * 4 : 0;
+}
+
+Fp8Ws layout_fp8(const cb_layer_config& c, int m, size_t base) {
+  const Dims D(c);
+  const size_t M = (size_t)std::max(m, 1);
+  Fp8Ws w{};
+  size_t off = base;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.codes = take(M * std::max(std::max(D.d, D.q_dim), D.F));
+  w.exps = take(M * 4);
+  w.prod = take(M * std::max((size_t)epilogue_ld(D.n_qkv()), (size_t)epilogue_ld(D.d)) * 4);
+  w.part = take(std::max(std::max(fp8_part_bytes((int)M, D.n_qkv(), D.d), fp8_part_bytes((int)M, D.d, D.q_dim)),
+                         std::max(fp8_part_bytes((int)M, 2 * D.F, D.d), fp8_part_bytes((int)M, D.d, D.F))));
+  w.total = off;
+  return w;
+}
+
+// Rows of A (bf16 [M][K]) quantized to E4M3 per row, times the 8-bit
+// weights [N][K], scaled by both row exponents, in fp32: in C (row stride
+// ldc) or, when K is split and ldc == N, left as the split partials, which
+// the epilogue kernels sum in split order.  *out / *splits say which.
+cb_status proj_fp8(const void* A, int M, int K, const uint8_t* w, const int32_t* we, int N, float* C, int ldc,
+                   const Fp8Ws& F8, void* ws, hipStream_t s, float** out, int* splits) {
+  uint8_t* codes = at<uint8_t>(ws, F8.codes);
+  int* exps = at<int>(ws, F8.exps);
+  cb_status st = hip_status(launch_quantize_rows(CB_BF16, A, M, K, codes, exps, s));
+  if (st) return st;
+  Fp8GemmArgs g{};
+  g.A = codes;
+  g.a_exp = exps;
+  g.B = w;
+  g.b_exp = we;
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ldc = ldc;
+  g.splits = fp8_splits(N, K);
+  g.part = at<float>(ws, F8.part);
+  g.keep_parts = g.splits > 1 && ldc == N;
+  *out = g.keep_parts ? g.part : C;
+  *splits = g.keep_parts ? g.splits : 1;
+  return hip_status(launch_gemm_fp8(g, CB_F32, s));
+}
+
+// u = silu(x W_gate^T) * (x W_up^T) (bf16 [M][F]) with 8-bit x rows and
+// weights w_gu = [W_gate; W_up], SwiGLU in the GEMM's epilogue
+cb_status proj_fp8_gated(const void* A, int M, int K, const uint8_t* w, const int32_t* we, int F, void* u,
+                         const Fp8Ws& F8, void* ws, hipStream_t s) {
+  uint8_t* codes = at<uint8_t>(ws, F8.codes);
+  int* exps = at<int>(ws, F8.exps);
+  cb_status st = hip_status(launch_quantize_rows(CB_BF16, A, M, K, codes, exps, s));
+  if (st) return st;
+  Fp8GemmArgs g{};
+  g.A = codes;
+  g.a_exp = exps;
+  g.B = w;
+  g.b_exp = we;
+  g.C = u;
+  g.M = M;
+  g.N = 2 * F;
+  g.K = K;
+  g.ldc = F;
+  g.splits = 1;
+  g.gated_F = F;
+  return hip_status(launch_gemm_fp8(g, CB_BF16, s));
+}
+
 // The part of a layer after attention: O projection + residual, RMSNorm,
 // SwiGLU MLP, down projection + residual.  resid rows: map(i) = m2[m1[i]].
 cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const Ws& L, void* ws, int m_out,
                      const void* hidden_in, int n_resid, const int* m1, const int* m2, void* hidden_out,
-                     hipStream_t s) {
+                     hipStream_t s, const cb_layer_weights_fp8* w8 = nullptr, const Fp8Ws* F8 = nullptr) {
   const Dims D(c);
   const int dt = c.dtype;
   // O projection + residual -> h (fp32)
@@ -220,8 +303,15 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   g.splits = gemm_splits(dt, gemm_n_tiles(dt, g.B, g.N), g.K);
   g.part = at<float>(ws, L.part);
   // ... and RMSNorm(h) -> hn
-  cb_status st = hip_status(
-      launch_gemm_resid_norm(dt, g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s));
+  cb_status st;
+  if (w8) {
+    st = proj_fp8(g.A, m_out, D.q_dim, w8->w_o, w8->e_o, D.d, at<float>(ws, F8->prod), epilogue_ld(D.d), *F8, ws,
+                  s, &g.part, &g.splits);
+    if (st) return st;
+    st = hip_status(launch_resid_norm_only(g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s));
+  } else {
+    st = hip_status(launch_gemm_resid_norm(dt, g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s));
+  }
   if (st) return st;
   // gate/up + SwiGLU -> u
   GemmArgs gu{};
@@ -238,7 +328,11 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   gu.epi.ld_out = D.F;
   gu.splits = gemm_splits(dt, gemm_n_tiles(dt, gu.B, 0), gu.K);
   gu.part = at<float>(ws, L.part);
-  st = hip_status(launch_gemm(dt, gu, s));
+  if (w8) {
+    st = proj_fp8_gated(gu.A, m_out, D.d, w8->w_gu, w8->e_gu, D.F, gu.epi.out, *F8, ws, s);
+  } else {
+    st = hip_status(launch_gemm(dt, gu, s));
+  }
   if (st) return st;
   // down projection + residual (h) -> hidden_out
   GemmArgs gd{};
@@ -256,6 +350,12 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   gd.epi.ld_out = D.d;
   gd.splits = gemm_splits(dt, gemm_n_tiles(dt, gd.B, gd.N), gd.K);
   gd.part = at<float>(ws, L.part);
+  if (w8) {
+    st = proj_fp8(gd.A, m_out, D.F, w8->w_down, w8->e_down, D.d, at<float>(ws, F8->prod), epilogue_ld(D.d), *F8,
+                  ws, s, &gd.part, &gd.splits);
+    if (st) return st;
+    return hip_status(launch_epilogue_only(gd, s));
+  }
   return hip_status(launch_gemm(dt, gd, s));
 }
 
@@ -483,7 +583,7 @@ namespace {
 cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const cb_rope_dev& rope, void* k_cache,
                     void* v_cache, int T, int n_ctx, int first_chunk_len, const int32_t* s_in, int m_in,
                     const void* hidden_in, const int32_t* in_rows, int k_out, void* hidden_out, float* dev_out,
-                    int32_t* s_out, void* ws, hipStream_t s) {
+                    int32_t* s_out, void* ws, hipStream_t s, const cb_layer_weights_fp8* w8 = nullptr) {
   const cb_layer_config* cfg = &c;
   const cb_layer_weights* wp = &w;
   const int n_query = T - n_ctx;
@@ -491,6 +591,7 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   const int m_out = std::min(k_out, n_cand) + n_query;
   const Dims D(c);
   const Ws L = layout(c, std::max(T, m_in), T);
+  const Fp8Ws F8 = layout_fp8(c, std::max(T, m_in), align256(L.total));
   const int dt = c.dtype;
   const int n_src = in_rows ? T : m_in;
   cb_status st;
@@ -509,7 +610,14 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   g.epi.v_cache = v_cache;
   g.epi.T = T;
   g.epi.dev_part = at<float>(ws, L.devp);
-  st = hip_status(launch_gemm(dt, g, s));
+  if (w8) {
+    st = proj_fp8(g.A, m_in, D.d, w8->w_qkv, w8->e_qkv, D.n_qkv(), at<float>(ws, F8.prod), epilogue_ld(D.n_qkv()),
+                  F8, ws, s, &g.part, &g.splits);
+    if (st) return st;
+    st = hip_status(launch_epilogue_only(g, s));
+  } else {
+    st = hip_status(launch_gemm(dt, g, s));
+  }
   if (st) return st;
   // 3. deviation sums + top-k + query rows
   SelectArgs sa{};
@@ -544,7 +652,8 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
   // 5. O projection, MLP
-  return layer_tail(c, w, L, ws, m_out, hidden_in, n_src, at<int>(ws, L.sel), in_rows, hidden_out, s);
+  return layer_tail(c, w, L, ws, m_out, hidden_in, n_src, at<int>(ws, L.sel), in_rows, hidden_out, s, w8,
+                    w8 ? &F8 : nullptr);
 }
 
 }  // namespace
@@ -577,6 +686,55 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   if (m_in == 0) return CB_OK;
   return cb::blend_run(*cfg, *w, *rope, k_cache, v_cache, T, n_ctx, first_chunk_len, s_in, m_in, hidden_in, in_rows,
                        k_out, hidden_out, dev_out, s_out, ws, (hipStream_t)stream);
+}
+
+extern "C" size_t cb_workspace_size_fp8(const cb_layer_config* cfg, int32_t T, int32_t m_max) {
+  if (check_cfg(cfg) != CB_OK || T < 0 || m_max < 0) return 0;
+  const int m = std::max(T, m_max);
+  return layout_fp8(*cfg, m, align256(layout(*cfg, m, T).total)).total;
+}
+
+extern "C" cb_status cb_blend_layer_fp8(const cb_layer_config* cfg, const cb_layer_weights_fp8* w8,
+                                        const cb_rope_dev* rope, void* k_cache, void* v_cache, int32_t T,
+                                        int32_t n_ctx, int32_t first_chunk_len, const int32_t* s_in, int32_t m_in,
+                                        const void* hidden_in, const int32_t* in_rows, int32_t k_out,
+                                        void* hidden_out, float* dev_out, int32_t* s_out, int32_t* m_out_host,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!w8) return CB_ERR_ARG;
+  {
+    const void* p[10] = {w8->attn_norm, w8->w_qkv, w8->e_qkv, w8->w_o,  w8->e_o,
+                         w8->mlp_norm,  w8->w_gu,  w8->e_gu,  w8->w_down, w8->e_down};
+    for (const void* x : p)
+      if (!x) return CB_ERR_ARG;
+    if (!aligned16(w8->w_qkv) || !aligned16(w8->w_o) || !aligned16(w8->w_gu) || !aligned16(w8->w_down))
+      return CB_ERR_ARG;
+  }
+  if (cfg->dtype != CB_BF16) return CB_ERR_UNSUPPORTED;
+  const Dims D(*cfg);
+  if (D.d % 16 || D.q_dim % 16 || D.F % 16) return CB_ERR_SHAPE;
+  if (!k_cache || !v_cache || !s_in || !hidden_in || !hidden_out || !s_out || !ws) return CB_ERR_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(hidden_in) || !aligned16(hidden_out) ||
+      !aligned16(ws))
+    return CB_ERR_ARG;
+  if (T <= 0 || n_ctx < 0 || first_chunk_len < 0 || m_in < 0 || k_out < 0) return CB_ERR_ARG;
+  if (n_ctx > T || first_chunk_len > n_ctx) return CB_ERR_SHAPE;
+  const int n_query = T - n_ctx;
+  const int n_cand = m_in - n_query;
+  if (n_cand < 0 || n_cand > n_ctx - first_chunk_len) return CB_ERR_SHAPE;
+  st = check_rope(rope, T);
+  if (st) return st;
+  if (ws_bytes < cb_workspace_size_fp8(cfg, T, m_in)) return CB_ERR_WORKSPACE;
+  const int m_out = std::min(k_out, n_cand) + n_query;
+  if (m_out_host) *m_out_host = m_out;
+  if (m_in == 0) return CB_OK;
+  // the norms as bf16-path weights (the projections come from w8)
+  cb_layer_weights wn{};
+  wn.attn_norm = w8->attn_norm;
+  wn.mlp_norm = w8->mlp_norm;
+  return cb::blend_run(*cfg, wn, *rope, k_cache, v_cache, T, n_ctx, first_chunk_len, s_in, m_in, hidden_in, in_rows,
+                       k_out, hidden_out, dev_out, s_out, ws, (hipStream_t)stream, w8);
 }
 
 extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_layer_weights* w,

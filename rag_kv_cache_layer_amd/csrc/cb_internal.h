@@ -254,6 +254,13 @@ int gemm_bn(int dtype);                               // N tile width
 int gemm_splits(int dtype, int N_tiles, int K);       // split-K choice (independent of M)
 int gemm_n_tiles(int dtype, const BOperand& B, int N);
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
+// The epilogue of g.epi.kind (QKV, RESID or STORE; bf16 cache) applied to a
+// product already in g.part (g.splits fp32 slices of row stride
+// epilogue_ld(g.N)), e.g. one written by the fp8 GEMM.
+hipError_t launch_epilogue_only(const GemmArgs& g, hipStream_t s);
+int epilogue_ld(int N);
+// ... the RESID epilogue into fp32 h followed by the RMSNorm of h into hn
+hipError_t launch_resid_norm_only(const GemmArgs& g, const float* gain, float eps, void* hn, hipStream_t s);
 // A residual projection into fp32 rows (epi.out) followed by the RMSNorm of
 // those rows into hn (the cache dtype), fused after split-K when possible.
 hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g, const float* gain, float eps, void* hn,
@@ -274,6 +281,8 @@ struct Fp8GemmArgs {
   int M, N, K, ldc;
   int splits;     // split-K factor (fp32 partials in part, summed in order)
   float* part;    // [splits][M][N]
+  int keep_parts; // splits > 1: leave the partials in part for the caller to sum
+  int gated_F;    // > 0: B = [W_gate; W_up] (2 gated_F rows) and C = silu(A W_gate^T) * (A W_up^T), bf16 [M][ldc]
 };
 int fp8_splits(int N, int K);
 hipError_t launch_quantize_rows(int src_dtype, const void* x, int rows, int cols, uint8_t* q, int* ex,

@@ -113,19 +113,21 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt,
     aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K) : kOOB;
     boff[j] = n0 + row < N ? (uint32_t)((int64_t)(n0 + row) * K) : kOOB;
   }
-  auto issue = [&](int stage, int k0) {
+  // row group j of the A and B tiles of one stage (two wave instructions)
+  auto issue_group = [&](int stage, int k0, int j) {
     char* sa = smem + stage * kQStage;
     char* sb = sa + QBM * QBK;
+    const int grp = w * 4 + j;
+    const int kk = k0 + lcol[j];
+    const bool kin = kk < ke;
+    const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk : kOOB;
+    const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+  };
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int grp = w * 4 + j;
-      const int kk = k0 + lcol[j];
-      const bool kin = kk < ke;
-      const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk : kOOB;
-      const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) issue_group(stage, k0, j);
   };
 
   f32x4_t acc[4][4];
@@ -150,11 +152,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt,
       bfr[i] = frag(sb, wn + i * 16 + fr);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, 127, 0,
                                                                       127);
+    }
   };
 
 #pragma unroll
@@ -207,7 +210,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt,
 }
 
 // gemm_fp8_big_kernel: the same product on 256x256 tiles for wide outputs
-// (enough tiles to fill the chip without split-K).  8 waves of 128x64, K
+// (enough tiles to fill the chip without split-K).  Gated mode (gate/up of a
+// SwiGLU MLP, B = [W_gate; W_up]): tile tn holds gate rows 128 tn .. +127 in
+// its first 128 columns and the same up rows in the last 128, and the
+// epilogue writes silu(gate) * up for those 128 features.  8 waves of 128x64, K
 // steps of 128 bytes, a two-stage LDS ring of 64 KB stages filled by
 // direct-to-LDS loads (the 128-byte row swizzle of the 128x128 kernel), with
 // the next stage's loads issued one 1 KB block per MFMA row.  A 256x256 tile
@@ -229,6 +235,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int
   const int m0 = tm * QLM, n0 = tn * QLN;
   const int M = g.M, N = g.N, K = g.K;
   const int nk = (K + QBK - 1) / QBK;
+  const int GF = g.gated_F;
+  // weight row of tile column c (-1 past the end)
+  auto brow_of = [&](int c) {
+    if (GF == 0) return n0 + c < N ? n0 + c : -1;
+    const int f = tn * (QLN / 2) + (c % (QLN / 2));
+    return f < GF ? (c < QLN / 2 ? f : GF + f) : -1;
+  };
 
   // DMA plan: block b of a stage holds tile rows 8b .. 8b+7 (A's 256 rows,
   // then B's); wave w fills blocks w + 8j; lane i fills slot i % 8 of row
@@ -244,8 +257,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int
     const bool is_a = blk < kQLBlocksA;
     const int row = (is_a ? blk : blk - kQLBlocksA) * 8 + (lane >> 3);
     lcol[j] = ((lane & 7) ^ ((row >> 1) & 7)) * 16;
-    const int grow = (is_a ? m0 : n0) + row;
-    off[j] = grow < (is_a ? M : N) ? (uint32_t)((int64_t)grow * K) : kOOB;
+    const int grow = is_a ? (m0 + row < M ? m0 + row : -1) : brow_of(row);
+    off[j] = grow >= 0 ? (uint32_t)((int64_t)grow * K) : kOOB;
   }
   auto issue_group = [&](int stage, int k0, int j) {
     const int blk = w + 8 * j;
@@ -308,8 +321,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn + j * 16 + fr;
-          const int eb = col < N ? g.b_exp[col] : 0;
+          const int br = brow_of(wn + j * 16 + fr);
+          const int eb = br >= 0 ? g.b_exp[br] : 0;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int rr = i * 16 + fc * 4 + v;   // row within the half
@@ -320,6 +333,26 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int
         }
     }
     __syncthreads();
+    if (GF > 0) {
+      // u = silu(gate) * up for features 128 tn .. +127, bf16
+      for (int idx = tid; idx < 128 * (QLN / 16); idx += 512) {
+        const int r = idx / (QLN / 16), c = (idx % (QLN / 16)) * 8;
+        const int row = m0 + half * 128 + r, f = tn * (QLN / 2) + c;
+        if (row >= M || f >= GF) continue;
+        const float* gp = Cs + r * QLCLD + c;
+        float o[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) o[x] = (gp[x] / (1.0f + expf(-gp[x]))) * gp[x + QLN / 2];
+        bf16_t* dst = (bf16_t*)g.C + (int64_t)row * g.ldc + f;
+        if (vec && f + 8 <= GF) {
+          store8(dst, o);
+        } else {
+          for (int x = 0; x < 8 && f + x < GF; ++x) Elem<bf16_t>::st(dst + x, o[x]);
+        }
+      }
+      __syncthreads();
+      continue;
+    }
     for (int idx = tid; idx < 128 * (QLN / 8); idx += 512) {
       const int r = idx / (QLN / 8), c = (idx % (QLN / 8)) * 8;
       const int row = m0 + half * 128 + r, col = n0 + c;
@@ -372,9 +405,10 @@ hipError_t launch_gemm_fp8(const Fp8GemmArgs& g, int out_dtype, hipStream_t s) {
   {
     // wide outputs: 256x256 tiles when they alone give ~3/4 of a wave of
     // workgroups per CU (the 128x128 kernel would not split K either)
-    const int lmt = (g.M + QLM - 1) / QLM, lnt = (g.N + QLN - 1) / QLN;
-    if (g.splits == 1 && lmt * lnt >= 192) {
-      LaunchScope ls("gemm_fp8_big", s);
+    const int lmt = (g.M + QLM - 1) / QLM;
+    const int lnt = g.gated_F > 0 ? (g.gated_F + QLN / 2 - 1) / (QLN / 2) : (g.N + QLN - 1) / QLN;
+    if (g.gated_F > 0 || (g.splits == 1 && lmt * lnt >= 192)) {
+      LaunchScope ls(g.gated_F > 0 ? "gemm_fp8_gateup" : "gemm_fp8_big", s);
       if (out_dtype == CB_BF16) gemm_fp8_big_kernel<bf16_t><<<lmt * lnt, 512, 0, s>>>(g, lmt, lnt);
       else gemm_fp8_big_kernel<float><<<lmt * lnt, 512, 0, s>>>(g, lmt, lnt);
       return hipGetLastError();
@@ -388,7 +422,7 @@ hipError_t launch_gemm_fp8(const Fp8GemmArgs& g, int out_dtype, hipStream_t s) {
     else gemm_fp8_kernel<float><<<grid, 256, 0, s>>>(g, mt, nt);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || g.splits <= 1) return e;
+  if (e != hipSuccess || g.splits <= 1 || g.keep_parts) return e;
   LaunchScope ls("gemm_fp8_split_sum", s);
   const int64_t n = (int64_t)g.M * g.N;
   const unsigned blocks = (unsigned)((n + 255) / 256);

@@ -770,6 +770,36 @@ int gemm_splits(int dtype, int n_tiles, int K) {
   return s;
 }
 
+hipError_t launch_epilogue_only(const GemmArgs& g0, hipStream_t s) {
+  if (g0.M <= 0) return hipSuccess;
+  GemmArgs g = g0;
+  const int ntiles = gemm_n_tiles(CB_BF16, g.B, g.N);
+  const int tpr = (g.epi.kind == EPI_SWIGLU ? BN / 2 : BN) / 8;
+  const dim3 rgrid((g.M + 256 / tpr - 1) / (256 / tpr), ntiles);
+  LaunchScope ls("epilogue", s);
+  switch (g.epi.kind) {
+    case EPI_QKV: splitk_epilogue_kernel<EPI_QKV><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+    case EPI_RESID: splitk_epilogue_kernel<EPI_RESID><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+    default: splitk_epilogue_kernel<EPI_STORE><<<rgrid, 256, 0, s>>>(g, ntiles); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_norm_only(const GemmArgs& g, const float* gain, float eps, void* hn, hipStream_t s) {
+  if (g.M <= 0) return hipSuccess;
+  if (g.epi.kind != EPI_RESID || !g.epi.out_f32 || g.N % 8 || g.N > 256 * 8 * kResidNormGroups ||
+      g.epi.ld_out != g.N) {
+    hipError_t e = launch_epilogue_only(g, s);
+    if (e != hipSuccess) return e;
+    return launch_rmsnorm(CB_BF16, true, g.epi.out, g.M, nullptr, nullptr, gain, hn, g.M, g.N, eps, s);
+  }
+  LaunchScope ls("resid_norm", s);
+  resid_norm_kernel<<<g.M, 256, 0, s>>>(g, gemm_n_tiles(CB_BF16, g.B, g.N), gain, eps, (bf16_t*)hn);
+  return hipGetLastError();
+}
+
+int epilogue_ld(int N) { return (N + BN - 1) / BN * BN; }
+
 hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g0, const float* gain, float eps, void* hn,
                                   hipStream_t s) {
   if (g0.M <= 0) return hipSuccess;

@@ -47,6 +47,11 @@ class LayerWeights(ctypes.Structure):
                 ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up", "w_down")]
 
 
+class LayerWeightsFp8(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "w_qkv", "e_qkv", "w_o", "e_o", "mlp_norm", "w_gu", "e_gu", "w_down", "e_down")]
+
+
 class RopeDev(ctypes.Structure):
     _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32)]
 
@@ -100,6 +105,9 @@ def lib() -> ctypes.CDLL:
         "cb_blend_stack_kv8": (I32, [CFG, I32, W, R, P, P, I64, P, P, P, P, I32, I32P, I32, I32, P, I32P, P, P, P,
                                      I32P, P, SZ, P, P]),
         "cb_kv_from_fp8": (I32, [CFG, R, P, P, P, P, I32, I32, I32, P, P, I64, I32, I32P, I32, I32, P]),
+        "cb_workspace_size_fp8": (SZ, [CFG, I32, I32]),
+        "cb_blend_layer_fp8": (I32, [CFG, ctypes.POINTER(LayerWeightsFp8), R, P, P, I32, I32, I32, P, I32, P, P, I32,
+                                     P, P, P, I32P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -258,6 +266,48 @@ class DeviceLayer:
                                       "w_down")])
 
 
+class DeviceLayerFp8:
+    """One layer's weights as 8-bit E4M3 codes + per-row exponents on the
+    device (cb_layer_weights_fp8): weights maps "w_qkv", "w_o", "w_gu",
+    "w_down" to (codes uint8 [rows][in], exps int32 [rows]) -- QKV rows are
+    W_q, W_k, W_v stacked, gate/up rows W_gate then W_up -- and "attn_norm",
+    "mlp_norm" to fp32 gains."""
+
+    NAMES = ("w_qkv", "w_o", "w_gu", "w_down")
+
+    def __init__(self, cfg: LayerConfig, weights: Dict[str, object], device="cuda"):
+        torch = _torch()
+        conv = lambda v: v if isinstance(v, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(v))
+        self.t = {}
+        for k in self.NAMES:
+            c, e = weights[k]
+            self.t[k] = conv(c).to(device=device, dtype=torch.uint8).contiguous()
+            self.t["e" + k[1:]] = conv(e).to(device=device, dtype=torch.int32).contiguous()
+        for k in ("attn_norm", "mlp_norm"):
+            self.t[k] = conv(weights[k]).to(device=device, dtype=torch.float32).contiguous()
+        self.struct = LayerWeightsFp8(*[self.t[n].data_ptr() for n in
+                                        ("attn_norm", "w_qkv", "e_qkv", "w_o", "e_o", "mlp_norm", "w_gu", "e_gu",
+                                         "w_down", "e_down")])
+
+    @classmethod
+    def quantized(cls, cfg: LayerConfig, layer: "DeviceLayer", device="cuda") -> "DeviceLayerFp8":
+        """Quantize a DeviceLayer's weights on the device (cb_quantize_fp8)."""
+        torch = _torch()
+        t = layer.t
+        w = {"w_qkv": quantize_fp8(torch.cat([t["w_q"], t["w_k"], t["w_v"]])),
+             "w_o": quantize_fp8(t["w_o"]), "w_gu": quantize_fp8(torch.cat([t["w_gate"], t["w_up"]])),
+             "w_down": quantize_fp8(t["w_down"]), "attn_norm": t["attn_norm"], "mlp_norm": t["mlp_norm"]}
+        return cls(cfg, w, device)
+
+
+def workspace_fp8(cfg: LayerConfig, T: int, m_max: int, device="cuda"):
+    torch = _torch()
+    n = int(lib().cb_workspace_size_fp8(ctypes.byref(cfg), T, m_max))
+    if n == 0:
+        raise CacheBlendError(1, "cb_workspace_size_fp8")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def workspace(cfg: LayerConfig, T: int, m_max: int, device="cuda"):
     torch = _torch()
     n = workspace_size(cfg, T, m_max)
@@ -309,6 +359,28 @@ def blend_layer(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, k_cache,
                                 _dptr(dev_out, "dev_out", torch.float32, m_in),
                                 _dptr(s_out, "s_out", torch.int32, m_exp), ctypes.byref(m_out),
                                 _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "cb_blend_layer")
+    return int(m_out.value)
+
+
+def blend_layer_fp8(cfg: LayerConfig, layer: DeviceLayerFp8, rope: DeviceRope, k_cache, v_cache, T: int, n_ctx: int,
+                    first_chunk_len: int, s_in, m_in: int, hidden_in, in_rows, k_out: int, hidden_out, dev_out,
+                    s_out, ws, stream=None) -> int:
+    """cb_blend_layer_fp8: blend_layer with 8-bit projections; returns m_out."""
+    torch = _torch()
+    dt = torch_dtype(cfg)
+    kv, d = cfg.n_kv_heads * cfg.head_dim, cfg.d_model
+    m_exp = max(expected_m_out(T, n_ctx, m_in, k_out), 0)
+    m_out = ctypes.c_int32(0)
+    _check(lib().cb_blend_layer_fp8(ctypes.byref(cfg), ctypes.byref(layer.struct), ctypes.byref(rope.struct),
+                                    _dptr(k_cache, "k_cache", dt, T * kv), _dptr(v_cache, "v_cache", dt, T * kv), T,
+                                    n_ctx, first_chunk_len, _dptr(s_in, "s_in", torch.int32, m_in), m_in,
+                                    _dptr(hidden_in, "hidden_in", dt, (T if in_rows is not None else m_in) * d),
+                                    _dptr(in_rows, "in_rows", torch.int32, m_in), k_out,
+                                    _dptr(hidden_out, "hidden_out", dt, m_exp * d),
+                                    _dptr(dev_out, "dev_out", torch.float32, m_in),
+                                    _dptr(s_out, "s_out", torch.int32, m_exp), ctypes.byref(m_out),
+                                    _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+           "cb_blend_layer_fp8")
     return int(m_out.value)
 
 

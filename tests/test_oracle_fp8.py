@@ -20,7 +20,8 @@
 import numpy as np
 import pytest
 
-from oracle import fp8
+from oracle import blend, fp8, layer
+from rag_kv_cache_layer_amd import synth
 
 
 def test_value_table():
@@ -107,3 +108,50 @@ def test_kv_expand_exact_and_per_head_scale():
     assert np.all(np.abs(z - y) <= 2.0 ** -4 * np.abs(y).max(2, keepdims=True))
     u = z.view(np.uint32)
     assert np.all((u & 0xFFFF) == 0)
+
+
+def _codes(rng, rows, cols):
+    c = rng.integers(0x10, 0x70, size=(rows, cols)).astype(np.uint8)
+    c |= (rng.integers(0, 2, size=(rows, cols)) << 7).astype(np.uint8)
+    return c, rng.integers(-6, 3, size=rows).astype(np.int32)
+
+
+def test_projector_exact_on_the_grid_and_rounds_activations():
+    rng = np.random.default_rng(4)
+    wc, we = _codes(rng, 16, 32)
+    xc, xe = _codes(rng, 5, 32)
+    xc[:, 0] = 0x7E                                       # each row reaches 448 * 2^e: its exponent is e
+    x = fp8.dequantize_rows(xc, xe).astype(np.float32)    # E4M3 values are bf16 numbers
+    lin = fp8.projector({"w_o": (wc, we)}, "bf16")
+    want = (x.astype(np.float64) @ fp8.dequantize_rows(wc, we).T).astype(np.float32)
+    assert np.array_equal(lin(x, "w_o"), want)
+    # activations are rounded to bf16 first: 1.1875 - 2^-12 rounds to 1.125 in
+    # E4M3 directly, but bf16 rounds it to 1.1875, the E4M3 midpoint of 1.125
+    # and 1.25, whose tie goes to the even code (1.25)
+    y = np.zeros((1, 32), np.float32)
+    y[0, 0] = 448.0                                       # row exponent 0
+    y[0, 1] = np.float32(1.1875 - 2.0 ** -12)
+    one_hot = np.zeros((32, 32), np.uint8)
+    one_hot[np.arange(32), np.arange(32)] = 0x38          # the identity (1.0) as codes
+    ident = fp8.projector({"w_o": (one_hot, np.zeros(32, np.int32))}, "bf16")
+    got = ident(y, "w_o")
+    assert got[0, 0] == 448.0 and got[0, 1] == 1.25
+    raw = fp8.projector({"w_o": (one_hot, np.zeros(32, np.int32))}, None)
+    assert raw(y, "w_o")[0, 1] == 1.125
+
+
+def test_fp8_layer_close_to_fp32_and_ratio_one_is_its_full_prefill():
+    p = synth.PRESETS["tiny_f32"]
+    w = synth.layer_weights(p, 0, 0)
+    lin = fp8.projector(fp8.quantize_layer(w), "bf16")
+    x = synth.random_normal(p, 0, (p.T, p.d_model), tag_layer=13)
+    k32, v32, y32 = layer.full_prefill(w, x, p)
+    k8, v8, y8 = layer.full_prefill(w, x, p, lin=lin)
+    rel = lambda a, b: float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+    for a, b in ((k8, k32), (v8, v32), (y8, y32)):
+        assert 1e-3 < rel(a, b) < 0.15
+    # r = 1: every candidate recomputed on the 8-bit layer's own full-prefill cache
+    L0 = 64
+    s_in = np.arange(L0, p.T)
+    out = blend.blend_layer(w, p, k8, v8, p.n_ctx, s_in, x[s_in], p.n_ctx, lin=lin)
+    assert rel(out["k_cache"], k8) < 1e-5 and rel(out["v_cache"], v8) < 1e-5 and rel(out["y"], y8[L0:]) < 1e-5

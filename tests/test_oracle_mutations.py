@@ -101,7 +101,7 @@ def test_rmsnorm_without_eps_inside_root_is_caught(monkeypatch):
 
 
 def test_swiglu_operands_swapped_is_caught(monkeypatch):
-    def out_rows(w, x, o, cfg, rowwise=False):
+    def out_rows(w, x, o, cfg, rowwise=False, lin=None):
         n = x.shape[0]
         h = x + layer.linear(o.reshape(n, -1), w["w_o"], rowwise)
         hn = layer.rmsnorm(h, w["mlp_norm"], cfg.rms_eps)
@@ -112,7 +112,7 @@ def test_swiglu_operands_swapped_is_caught(monkeypatch):
 
 
 def test_dropped_attention_residual_is_caught(monkeypatch):
-    def out_rows(w, x, o, cfg, rowwise=False):
+    def out_rows(w, x, o, cfg, rowwise=False, lin=None):
         n = x.shape[0]
         h = layer.linear(o.reshape(n, -1), w["w_o"], rowwise)
         hn = layer.rmsnorm(h, w["mlp_norm"], cfg.rms_eps)
