@@ -149,3 +149,47 @@ def test_other_calls_argument_errors(cblib):
 def test_profile_without_launches(cblib):
     F.profile_begin()
     assert F.profile_end() == {}
+
+
+def test_8bit_calls_argument_errors(cblib):
+    L, cfg = cblib, _cfg()
+    rope_ok = F.RopeDev(FAKE, FAKE, 4096)
+    w8 = F.LayerWeightsFp8(*([FAKE] * 10))
+    m = ctypes.c_int32(-7)
+
+    def blend8(c=cfg, w=w8, ws_bytes=1 << 40):
+        return L.cb_blend_layer_fp8(ctypes.byref(c), ctypes.byref(w) if w is not None else None,
+                                    ctypes.byref(rope_ok), FAKE, FAKE, 100, 90, 30, FAKE, 70, FAKE, None, 9, FAKE,
+                                    None, FAKE, ctypes.byref(m), FAKE, ws_bytes, None)
+    assert blend8(w=None) == 1
+    assert blend8(w=F.LayerWeightsFp8(*([FAKE] * 9 + [0]))) == 1                  # null e_down
+    assert blend8(w=F.LayerWeightsFp8(FAKE, FAKE + 8, *([FAKE] * 8))) == 1        # misaligned codes
+    assert blend8(c=_cfg(dtype="f32")) == 5
+    assert blend8(c=_cfg(d_model=520)) == 2                                        # d not a multiple of 16
+    assert blend8(ws_bytes=1000) == 4
+    assert m.value == -7
+    assert int(L.cb_workspace_size_fp8(ctypes.byref(cfg), 100, 100)) > F.workspace_size(cfg, 100, 100)
+    offs = (ctypes.c_int32 * 3)(0, 40, 90)
+    kv = L.cb_kv_from_fp8
+    assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), None, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100, offs,
+              2, 1, None) == 1
+    assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE + 4, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100,
+              offs, 2, 1, None) == 1                                               # misaligned codes
+    assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 50, 51, FAKE, FAKE, 0, 100, offs,
+              2, 1, None) == 2                                                     # rows past T
+    short = F.RopeDev(FAKE, FAKE, 40)
+    assert kv(ctypes.byref(cfg), ctypes.byref(short), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100, offs,
+              2, 1, None) == 2                                                     # table too short for the shift
+    cf72 = _cfg(dtype="f32", head_dim=72, n_q_heads=8, n_kv_heads=8, d_model=576)
+    assert F.workspace_size(cf72, 10, 10) > 0
+    assert kv(ctypes.byref(cf72), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100,
+              offs, 2, 1, None) == 2                                               # head_dim not a multiple of 16
+    many = (ctypes.c_int32 * 258)(*range(258))
+    assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 300, many,
+              257, 1, None) == 5
+    # the 8-bit stack needs all four sources
+    ks = (ctypes.c_int32 * 2)(10, 10)
+    Wl = (F.LayerWeights * 2)(F.LayerWeights(*([FAKE] * 9)), F.LayerWeights(*([FAKE] * 9)))
+    assert L.cb_blend_stack_kv8(ctypes.byref(cfg), 2, Wl, ctypes.byref(rope_ok), FAKE, FAKE, 100 * 128, FAKE, None,
+                                FAKE, FAKE, 100, offs, 2, 1, FAKE, ks, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None,
+                                None) == 1
