@@ -41,10 +41,11 @@
  *    synchronisation; results are ready when the stream has drained.
  *  - Errors are returned as cb_status; nothing aborts or throws across the
  *    ABI.  Argument and shape checks happen on the host before anything is
- *    enqueued.  Device index arrays are not read on the host: out-of-range
- *    entries are skipped by the kernels' bounds checks and make the results
- *    unspecified, never an out-of-bounds access.  A failed HIP launch returns
- *    CB_ERR_HIP and its code is kept per thread (cb_last_hip_error).
+ *    enqueued.  Device index arrays are not read on the host (unless validate
+ *    mode is on, cb_set_validate): out-of-range entries are skipped by the
+ *    kernels' bounds checks and make the results unspecified, never an
+ *    out-of-bounds access.  A failed HIP launch returns CB_ERR_HIP and its
+ *    code is kept per thread (cb_last_hip_error).
  *  - Calls that share a workspace or a cache must not overlap in time.
  */
 #ifndef CACHEBLEND_H
@@ -61,7 +62,7 @@ typedef enum {
   CB_OK = 0,
   CB_ERR_ARG = 1,          /* null pointer, negative size, bad enum            */
   CB_ERR_SHAPE = 2,        /* inconsistent geometry or head layout             */
-  CB_ERR_INDEX = 3,        /* reserved: index validation                       */
+  CB_ERR_INDEX = 3,        /* an index array failed validation (validate mode) */
   CB_ERR_WORKSPACE = 4,    /* workspace smaller than cb_workspace_size()       */
   CB_ERR_UNSUPPORTED = 5,  /* shape the gfx950 kernels do not handle           */
   CB_ERR_HIP = 6           /* a HIP runtime call or launch failed              */
@@ -160,6 +161,18 @@ const char* cb_status_string(cb_status s);
 
 /* hipError_t of the last failed HIP call on this thread (0 if none). */
 int32_t cb_last_hip_error(void);
+
+/* Validate mode for the calls this thread makes (off by default); returns
+ * the previous setting.  When on, cb_blend_layer, cb_blend_layer_fp8,
+ * cb_blend_batch and cb_select_hkvd first copy their device index arrays
+ * to the host (synchronising `stream`, since earlier work on it may produce
+ * them) and check them before enqueuing anything: CB_ERR_INDEX when s_in is
+ * not strictly ascending, has a row below first_chunk_len or at/after T, or
+ * lacks one of the query rows n_ctx .. T-1, when an in_rows entry is outside
+ * [0, T), or when a cand_rows entry is outside [0, T); CB_ERR_ARG when a
+ * deviation array given as input (k_new == NULL) holds a NaN (section 4.3's
+ * ranking needs ordered values). */
+int32_t cb_set_validate(int32_t on);
 
 /* Kernel timing.  Between cb_profile_begin and cb_profile_end every kernel
  * the library launches from this thread is bracketed by two hipEvents

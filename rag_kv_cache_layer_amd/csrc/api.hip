@@ -32,6 +32,7 @@ namespace cb {
 namespace {
 
 thread_local int32_t t_last_hip = 0;
+thread_local bool t_validate = false;
 
 struct ProfRec {
   const char* name;
@@ -465,6 +466,56 @@ extern "C" const char* cb_status_string(cb_status s) {
 
 extern "C" int32_t cb_last_hip_error(void) { return t_last_hip; }
 
+extern "C" int32_t cb_set_validate(int32_t on) {
+  const int32_t prev = t_validate ? 1 : 0;
+  t_validate = on != 0;
+  return prev;
+}
+
+namespace cb {
+namespace {
+
+// Copy n int32 (or float) values from the device after the stream's earlier
+// work; false on a HIP failure (recorded).
+template <typename T>
+bool fetch(std::vector<T>& out, const T* dev, int n, hipStream_t s) {
+  out.resize(n > 0 ? n : 0);
+  if (n <= 0) return true;
+  if (hip_status(hipMemcpyAsync(out.data(), dev, (size_t)n * sizeof(T), hipMemcpyDeviceToHost, s)) ||
+      hip_status(hipStreamSynchronize(s)))
+    return false;
+  return true;
+}
+
+// s_in of one request: strictly ascending, within [first_chunk_len, T), and
+// every query row n_ctx .. T-1 present (they are then its last T - n_ctx
+// entries); in_rows within [0, n_src).
+cb_status check_rows(const int32_t* s_in, int m_in, int T, int n_ctx, int first_chunk_len) {
+  for (int i = 0; i < m_in; ++i) {
+    if (s_in[i] < first_chunk_len || s_in[i] >= T) return CB_ERR_INDEX;
+    if (i > 0 && s_in[i] <= s_in[i - 1]) return CB_ERR_INDEX;
+  }
+  const int q = T - n_ctx;
+  for (int j = 0; j < q; ++j)
+    if (s_in[m_in - q + j] != n_ctx + j) return CB_ERR_INDEX;
+  return CB_OK;
+}
+
+cb_status validate_blend(const int32_t* s_in_d, int m_in, const int32_t* in_rows_d, int T, int n_ctx,
+                         int first_chunk_len, hipStream_t s) {
+  std::vector<int32_t> rows;
+  if (!fetch(rows, s_in_d, m_in, s)) return CB_ERR_HIP;
+  cb_status st = check_rows(rows.data(), m_in, T, n_ctx, first_chunk_len);
+  if (st || !in_rows_d) return st;
+  if (!fetch(rows, in_rows_d, m_in, s)) return CB_ERR_HIP;
+  for (int i = 0; i < m_in; ++i)
+    if (rows[i] < 0 || rows[i] >= T) return CB_ERR_INDEX;
+  return CB_OK;
+}
+
+}  // namespace
+}  // namespace cb
+
 // ---------------------------------------------------------------------------
 // kernel timing
 // ---------------------------------------------------------------------------
@@ -561,6 +612,20 @@ extern "C" cb_status cb_select_hkvd(const cb_layer_config* cfg, const void* k_ne
   if (n == 0) return CB_OK;
   hipStream_t s = (hipStream_t)stream;
   const Dims D(*cfg);
+  if (t_validate) {
+    if (k_new) {
+      std::vector<int32_t> rows;
+      if (!cand_rows) return CB_ERR_ARG;
+      if (!cb::fetch(rows, cand_rows, n, s)) return CB_ERR_HIP;
+      for (int i = 0; i < n; ++i)
+        if (rows[i] < 0 || rows[i] >= T) return CB_ERR_INDEX;
+    } else {
+      std::vector<float> d;
+      if (!cb::fetch(d, (const float*)dev, n, s)) return CB_ERR_HIP;
+      for (int i = 0; i < n; ++i)
+        if (std::isnan(d[i])) return CB_ERR_ARG;
+    }
+  }
   if (k_new) {
     st = hip_status(launch_kdev(cfg->dtype, k_new, k_ref, cand_rows, n, D.kv_dim, T, dev, s));
     if (st) return st;
@@ -681,6 +746,10 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   st = check_rope(rope, T);
   if (st) return st;
   if (ws_bytes < cb_workspace_size(cfg, T, m_in)) return CB_ERR_WORKSPACE;
+  if (t_validate && m_in > 0) {
+    st = cb::validate_blend(s_in, m_in, in_rows, T, n_ctx, first_chunk_len, (hipStream_t)stream);
+    if (st) return st;
+  }
   const int m_out = std::min(k_out, n_cand) + n_query;
   if (m_out_host) *m_out_host = m_out;
   if (m_in == 0) return CB_OK;
@@ -726,6 +795,10 @@ extern "C" cb_status cb_blend_layer_fp8(const cb_layer_config* cfg, const cb_lay
   st = check_rope(rope, T);
   if (st) return st;
   if (ws_bytes < cb_workspace_size_fp8(cfg, T, m_in)) return CB_ERR_WORKSPACE;
+  if (t_validate && m_in > 0) {
+    st = cb::validate_blend(s_in, m_in, in_rows, T, n_ctx, first_chunk_len, (hipStream_t)stream);
+    if (st) return st;
+  }
   const int m_out = std::min(k_out, n_cand) + n_query;
   if (m_out_host) *m_out_host = m_out;
   if (m_in == 0) return CB_OK;
@@ -1158,6 +1231,17 @@ extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_w
   st = check_rope(rope, T_max);
   if (st) return st;
   if (ws_bytes < cb_workspace_size(cfg, T_max, M_in)) return CB_ERR_WORKSPACE;
+  if (t_validate && M_in > 0) {
+    std::vector<int32_t> rows;
+    if (!cb::fetch(rows, s_in, M_in, (hipStream_t)stream)) return CB_ERR_HIP;
+    int off = 0;
+    for (int r = 0; r < n_req; ++r) {
+      const cb_blend_request& q = reqs[r];
+      st = cb::check_rows(rows.data() + off, q.m_in, q.T, q.n_ctx, q.first_chunk_len);
+      if (st) return st;
+      off += q.m_in;
+    }
+  }
   if (m_out_host)
     for (int r = 0; r < n_req; ++r) m_out_host[r] = m_out[r];
   if (M_in == 0) return CB_OK;

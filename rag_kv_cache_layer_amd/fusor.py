@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         "cb_workspace_size": (SZ, [CFG, I32, I32]),
         "cb_status_string": (ctypes.c_char_p, [I32]),
         "cb_last_hip_error": (I32, []),
+        "cb_set_validate": (I32, [I32]),
         "cb_profile_begin": (I32, []),
         "cb_profile_end": (I32, [ctypes.POINTER(KernelStat), I32]),
         "cb_rope_shift": (I32, [CFG, R, P, I64, I32, I32, I32P, I32, P]),
@@ -115,6 +116,11 @@ def lib() -> ctypes.CDLL:
         f.argtypes = args
     _lib = L
     return L
+
+
+def set_validate(on: bool) -> bool:
+    """cb_set_validate for this thread; returns the previous setting."""
+    return bool(lib().cb_set_validate(1 if on else 0))
 
 
 def _check(status: int, where: str):

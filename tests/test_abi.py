@@ -193,3 +193,9 @@ def test_8bit_calls_argument_errors(cblib):
     assert L.cb_blend_stack_kv8(ctypes.byref(cfg), 2, Wl, ctypes.byref(rope_ok), FAKE, FAKE, 100 * 128, FAKE, None,
                                 FAKE, FAKE, 100, offs, 2, 1, FAKE, ks, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None,
                                 None) == 1
+
+
+def test_validate_switch(cblib):
+    assert F.set_validate(True) is False
+    assert F.set_validate(False) is True
+    assert F.set_validate(False) is False
