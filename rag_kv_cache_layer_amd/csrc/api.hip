@@ -711,7 +711,7 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   aa.n_q = cfg->n_q_heads;
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
-  aa.key_split = attn_key_split(dt, m_out, cfg->n_q_heads, cfg->n_kv_heads);
+  aa.key_split = attn_key_split(dt, m_out, cfg->n_kv_heads, T);
   aa.o_part = at<float>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
@@ -853,7 +853,7 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   aa.n_q = cfg->n_q_heads;
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
-  aa.key_split = attn_key_split(dt, T, cfg->n_q_heads, cfg->n_kv_heads);
+  aa.key_split = attn_key_split(dt, T, cfg->n_kv_heads, T);
   aa.o_part = at<float>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
@@ -1312,7 +1312,7 @@ extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_w
   aa.n_q = c.n_q_heads;
   aa.n_kv = c.n_kv_heads;
   aa.hd = D.hd;
-  aa.key_split = attn_key_split(dt, tiles * kAttnRowTile, c.n_q_heads, c.n_kv_heads);
+  aa.key_split = attn_key_split(dt, tiles * kAttnRowTile, c.n_kv_heads, T_max);
   aa.o_part = at<float>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   aa.req.n = n_req;

@@ -35,6 +35,7 @@
 // result still does not either.
 //
 // fp32 path: one wave per (row, head); scores in LDS, two-pass softmax.
+#include <algorithm>
 #include <climits>
 
 #include "cb_internal.h"
@@ -64,7 +65,7 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 #ifndef CB_ATTN_SPLIT
 #define CB_ATTN_SPLIT 512
 #endif
-constexpr int kKeySplit = CB_ATTN_SPLIT;   // key-split boundary (multiple of kKeyTile)
+constexpr int kKeySplit = CB_ATTN_SPLIT;   // smallest key split (multiple of kKeyTile)
 static_assert(kKeySplit % 64 == 0 && kKeySplit >= 512, "the partial buffers are sized for splits of >= 512 keys");
 
 // One wave instruction: 16 bytes per lane from the buffer at byte offset
@@ -513,11 +514,18 @@ hipError_t launch_bf16_hd(const AttnArgs& a, hipStream_t s, float scale_log2) {
 
 }  // namespace
 
-int attn_key_split(int dtype, int m, int n_q, int n_kv) {
-  (void)n_q;
+int attn_key_split(int dtype, int m, int n_kv, int T) {
   if (dtype != CB_BF16) return 0;
-  const int blocks = (m + kRowTile - 1) / kRowTile * n_kv;
-  return blocks < 512 ? kKeySplit : 0;
+  const int groups = (m + kRowTile - 1) / kRowTile * n_kv;
+  if (groups >= 512) return 0;
+  // about 1.5 workgroups per slot (two per CU): the keys in ~768 / groups
+  // parts, each a whole number of key tiles and at least kKeySplit keys (the
+  // partial buffers hold T / kKeySplit splits).  At the 8B layer (128
+  // groups, T = 3104) that is 6 parts of 576 keys: attention + merge 47 us,
+  // against 55 us with 7 parts of 512 and 52 us with 4 of 832.
+  const int parts = std::max(1, (768 + groups / 2) / groups);
+  const int per = (T + parts - 1) / parts;
+  return std::max(kKeySplit, (per + 63) / 64 * 64);
 }
 
 size_t attn_part_rows(int n_q, int n_kv) {

@@ -304,9 +304,10 @@ struct AttnArgs {
   float* ml_part;         // [T / key_split][m][n_q][2] running max (log2 units) and sum
   ReqTable req;           // several requests: row ranges, row tiles, K/V and T per request (T = max)
 };
-// Key-split length used for m query rows (0 = none); chosen from the row and
-// head counts only.  attn_part_rows bounds the m for which it is non-zero.
-int attn_key_split(int dtype, int m, int n_q, int n_kv);
+// Key-split length used for m query rows over T keys (0 = none): a multiple
+// of 64, at least 512; chosen from the row, head and key counts only.
+// attn_part_rows bounds the m for which it is non-zero.
+int attn_key_split(int dtype, int m, int n_kv, int T);
 size_t attn_part_rows(int n_q, int n_kv);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
