@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--analytics", action="store_true",
                     help="also run the deviation analytics (attention deviation vs r, deviation "
                          "concentration, neighbour-layer rank correlation) on the 32-layer stack")
+    ap.add_argument("--llama70b", action="store_true",
+                    help="also time the blend call of one Llama-70B-shaped layer (8 x 500 + 32 tokens, r=0.15)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 512 MiB device-to-device copy first (a known-size reference "
                          "for the HBM byte counters)")
@@ -283,6 +285,8 @@ def main():
         extra["pipeline"] = pipeline_measure(seed)
     if args.analytics:
         extra["analytics"] = analytics_measure(seed)
+    if args.llama70b:
+        extra["llama70b_layer"] = layer70b_measure(seed, args.steps)
     if args.fp8:
         extra["fp8"] = fp8_measure(p, m, args.steps)
         # the same step with the layer's projections in 8 bits (cb_blend_layer_fp8)
@@ -391,6 +395,80 @@ def shift_stack_measure(reps=6):
     return {"layers": L, "bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "copy_same_bytes_gbs": round(nbytes / (cms * 1e-3) / 1e9, 1)}
+
+
+def layer70b_measure(seed, steps):
+    """The blend call of one 70B-shaped layer (d 8192, 64/8 heads x 128, FFN
+    28672; 8 x 500 + 32 tokens, r = 0.15) with seeded N(0, 0.02) weights drawn
+    on the device, seeded N(0, 1) cached K/V and layer inputs: the select call
+    once (untimed) for the kept set, then cb_rope_shift + the blend call on
+    that set, as for the 8B layer."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+    p = synth.PRESETS["llama70b_stack"]
+    cfg = F.config_of(p)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2000 + seed)
+    shapes = {"w_q": (p.q_dim, p.d_model), "w_k": (p.kv_dim, p.d_model), "w_v": (p.kv_dim, p.d_model),
+              "w_o": (p.d_model, p.q_dim), "w_gate": (p.ffn_dim, p.d_model), "w_up": (p.ffn_dim, p.d_model),
+              "w_down": (p.d_model, p.ffn_dim)}
+    w = {n: (torch.randn(s, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for n, s in shapes.items()}
+    w["attn_norm"] = torch.ones(p.d_model, device="cuda")
+    w["mlp_norm"] = torch.ones(p.d_model, device="cuda")
+    layer = F.DeviceLayer(cfg, w)
+    del w
+    T, n_ctx, kvd, d = p.T, p.n_ctx, p.kv_dim, p.d_model
+    offs = synth.chunk_offsets(p, range(p.n_chunks))
+    L0 = int(offs[1])
+    k = F.num_selected(p.r_e4, n_ctx, n_ctx - L0)
+    rope = F.DeviceRope(cfg, T)
+    ws = F.workspace(cfg, T, T)
+    k_pre = torch.randn((T, kvd), generator=g, device="cuda").to(torch.bfloat16)
+    v_pre = torch.randn((T, kvd), generator=g, device="cuda").to(torch.bfloat16)
+    x = torch.randn((T, d), generator=g, device="cuda").to(torch.bfloat16)
+    kc, vc = k_pre.clone(), v_pre.clone()
+    F.rope_shift(cfg, rope, kc, T * kvd, 1, T, offs)
+    s_all = torch.arange(L0, T, dtype=torch.int32, device="cuda")
+    m = F.expected_m_out(T, n_ctx, T - L0, k)
+    S = torch.empty(m, dtype=torch.int32, device="cuda")
+    hout = torch.empty((m, d), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty(T - L0, dtype=torch.float32, device="cuda")
+    F.blend_layer(cfg, layer, rope, kc, vc, T, n_ctx, L0, s_all, T - L0, x, s_all, k, hout, dv, S, ws)
+    torch.cuda.synchronize()
+    so = torch.empty(m, dtype=torch.int32, device="cuda")
+    kb, vb = k_pre.clone(), v_pre.clone()
+
+    def step():
+        F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
+        F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, x, S, k, hout, dv, so, ws)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    F.profile_begin()
+    for _ in range(steps):
+        step()
+    st = F.profile_end()
+    torch.cuda.synchronize()
+    flops = layer_flops(p, m, m, so.cpu().numpy())
+    kern = {}
+    for name, e in st.items():
+        avg = e["total_ms"] / e["launches"]
+        kern[name] = {"avg_ms": round(avg, 5)}
+        if name in flops:
+            kern[name]["frac_mfma"] = round(flops[name] / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    total = sum(flops.values())
+    return {"workload": "llama70b_layer: 8x500-token chunks + 32-token query (T=4032), r=0.15, "
+                        f"k={k} + 32 query rows; d=8192, 64q/8kv heads x128, ffn 28672",
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "layer_tflops": round(total / (ms * 1e-3) / 1e12, 1),
+            "layer_frac_mfma": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "kernels": kern}
 
 
 def kv_expand_measure(reps=6):
