@@ -111,3 +111,36 @@ def test_select_validation(validating):
     F.select_hkvd(cfg, kn, kr, T, rows, n, k, torch.zeros(n, device="cuda"), sel, ws)
     torch.cuda.synchronize()
     assert sel.cpu().numpy().tolist() == list(range(k))       # all deviations 0: the first k rows
+
+
+def test_batch_validation(validating):
+    """Two requests; the second one's rows run past its own cache."""
+    need_gpu()
+    case, cfg, layer, rope, ws = _setup()
+    T, n_ctx, L0 = P.T, P.n_ctx, case["L0"]
+    reqs, rows = [], []
+    for j in range(2):
+        reqs.append(dict(k_cache=dev(case["k"], torch.bfloat16), v_cache=dev(case["v"], torch.bfloat16), T=T,
+                         n_ctx=n_ctx, first_chunk_len=L0, m_in=T - L0, k_out=20))
+        rows.append(np.arange(L0, T))
+    bad = [r.copy() for r in rows]
+    bad[1][4] = bad[1][3]                                                   # a repeated row
+    m_tot = 2 * (T - L0)
+    ws2 = F.workspace(cfg, T, m_tot)
+    for s_list, want in ((bad, 3), (rows, 0)):
+        s_t = dev(np.concatenate(s_list).astype(np.int32), torch.int32)
+        hid = dev(np.concatenate([case["hidden"][r] for r in rows]), torch.bfloat16)
+        hout = torch.full((m_tot, P.d_model), 7.0, dtype=torch.bfloat16, device="cuda")
+        dv = torch.full((m_tot,), 7.0, dtype=torch.float32, device="cuda")
+        so = torch.full((m_tot,), -5, dtype=torch.int32, device="cuda")
+        try:
+            F.blend_batch(cfg, layer, rope, reqs, s_t, hid, hout, dv, so, ws2)
+            st = 0
+        except F.CacheBlendError as e:
+            st = e.status
+        torch.cuda.synchronize()
+        assert st == want
+        if want:
+            assert torch.all(so == -5) and torch.all(dv == 7.0)
+        else:
+            assert torch.all(so[:2 * (20 + T - n_ctx)] >= L0)
