@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--analytics", action="store_true",
                     help="also run the deviation analytics (attention deviation vs r, deviation "
                          "concentration, neighbour-layer rank correlation) on the 32-layer stack")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the blend step and full prefill of the 8B layer over 4/16/32 chunks x 512 + 64 "
+                         "tokens at r = 0.05, 0.10, 0.15, 0.30, 1.0")
     ap.add_argument("--llama70b", action="store_true",
                     help="also time the blend call of one Llama-70B-shaped layer (8 x 500 + 32 tokens, r=0.15)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -287,6 +290,8 @@ def main():
         extra["analytics"] = analytics_measure(seed)
     if args.llama70b:
         extra["llama70b_layer"] = layer70b_measure(seed, args.steps)
+    if args.sweep:
+        extra["sweep"] = sweep_measure(seed, min(args.steps, 20))
     if args.fp8:
         extra["fp8"] = fp8_measure(p, m, args.steps)
         # the same step with the layer's projections in 8 bits (cb_blend_layer_fp8)
@@ -395,6 +400,81 @@ def shift_stack_measure(reps=6):
     return {"layers": L, "bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "copy_same_bytes_gbs": round(nbytes / (cms * 1e-3) / 1e9, 1)}
+
+
+def sweep_measure(seed, steps):
+    """The 8B-shaped layer over n x 512 context tokens + 64 query tokens (chunk
+    order permuted), n = 4, 16, 32, at recompute ratios r = 0.05 .. 1: for each
+    point the select call (untimed) picks S, then cb_rope_shift + the blend
+    call on S is timed, next to a full prefill of the same layer over all T
+    rows (the full KV recompute baseline).  Seeded N(0, 0.02) weights drawn
+    on the device, seeded N(0, 1) cached K/V and layer inputs."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+    base = synth.sweep_preset(4, 1500)
+    cfg = F.config_of(base)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3000 + seed)
+    shapes = {"w_q": (base.q_dim, base.d_model), "w_k": (base.kv_dim, base.d_model),
+              "w_v": (base.kv_dim, base.d_model), "w_o": (base.d_model, base.q_dim),
+              "w_gate": (base.ffn_dim, base.d_model), "w_up": (base.ffn_dim, base.d_model),
+              "w_down": (base.d_model, base.ffn_dim)}
+    w = {n: (torch.randn(s, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for n, s in shapes.items()}
+    w["attn_norm"] = torch.ones(base.d_model, device="cuda")
+    w["mlp_norm"] = torch.ones(base.d_model, device="cuda")
+    layer = F.DeviceLayer(cfg, w)
+    del w
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    out = []
+    for n_chunks in (4, 16, 32):
+        p = synth.sweep_preset(n_chunks, 1500)
+        T, n_ctx, kvd, d = p.T, p.n_ctx, p.kv_dim, p.d_model
+        offs = synth.chunk_offsets(p, synth.chunk_order(p, seed))
+        L0 = int(offs[1])
+        rope = F.DeviceRope(cfg, T)
+        ws = F.workspace(cfg, T, T)
+        k_pre = torch.randn((T, kvd), generator=g, device="cuda").to(torch.bfloat16)
+        v_pre = torch.randn((T, kvd), generator=g, device="cuda").to(torch.bfloat16)
+        x = torch.randn((T, d), generator=g, device="cuda").to(torch.bfloat16)
+        kf, vf = torch.empty_like(k_pre), torch.empty_like(v_pre)
+        yf = torch.empty_like(x)
+        t_full = timed(lambda: F.full_prefill_layer(cfg, layer, rope, x, T, 0, kf, vf, yf, ws), max(steps // 4, 2))
+        s_all = torch.arange(L0, T, dtype=torch.int32, device="cuda")
+        dv = torch.empty(T - L0, dtype=torch.float32, device="cuda")
+        for r_e4 in (500, 1000, 1500, 3000, 10000):
+            k = F.num_selected(r_e4, n_ctx, n_ctx - L0)
+            m = F.expected_m_out(T, n_ctx, T - L0, k)
+            S = torch.empty(m, dtype=torch.int32, device="cuda")
+            hout = torch.empty((m, d), dtype=torch.bfloat16, device="cuda")
+            kc, vc = k_pre.clone(), v_pre.clone()
+            F.rope_shift(cfg, rope, kc, T * kvd, 1, T, offs)
+            F.blend_layer(cfg, layer, rope, kc, vc, T, n_ctx, L0, s_all, T - L0, x, s_all, k, hout, dv, S, ws)
+            torch.cuda.synchronize()
+            so = torch.empty(m, dtype=torch.int32, device="cuda")
+            kb, vb = k_pre.clone(), v_pre.clone()
+
+            def step():
+                F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
+                F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, x, S, k, hout, dv, so, ws)
+
+            ms = timed(step, steps)
+            out.append({"chunks": n_chunks, "T": T, "r": r_e4 / 1e4, "k": k, "ms": round(ms, 4),
+                        "tokens_per_s": round(T / (ms * 1e-3), 1), "full_prefill_ms": round(t_full, 4),
+                        "speedup_vs_full_prefill": round(t_full / ms, 2)})
+            del S, hout, kc, vc, so, kb, vb
+        del ws, k_pre, v_pre, x, kf, vf, yf, rope
+        torch.cuda.empty_cache()
+    return out
 
 
 def layer70b_measure(seed, steps):
