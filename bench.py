@@ -14,7 +14,7 @@ keys (cb_rope_shift) followed by the selective recompute of the HKVD rows
 scatter, top-k, partial causal GQA attention, O projection, SwiGLU MLP).
 value = context tokens blended per second = T / step time.
 
-Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -103,7 +103,7 @@ def layer_flops(p, m_in, m_out, positions):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library runs on one GPU", file=sys.stderr)
         sys.exit(2)
     import torch
     from rag_kv_cache_layer_amd import fusor as F

@@ -2,7 +2,7 @@
 infrastructure only).
 
 The paper serves its larger models with 8-bit weights (CacheBlend section 7,
-models).  This build's reading: OCP fp8 E4M3 (1 sign, 4 exponent bits with
+models).  The reading taken here: OCP fp8 E4M3 (1 sign, 4 exponent bits with
 bias 7, 3 mantissa bits; largest finite value 448, no infinities) with one
 power-of-two scale per matrix row, so that scaling is exact and only the
 rounding to E4M3 loses information:

@@ -58,7 +58,7 @@ def test_small_stack_matches_oracle_and_layer_calls():
         assert rel_err(host(Kd[l]), want["K"][l]) < 2e-2, l
         assert rel_err(host(Vd[l]), want["V"][l]) < 2e-2, l
     assert rel_err(host(out[-1]["y"]), want["y"]) < 2e-2
-    # the driver is exactly the per-layer calls
+    # fusor.blend_stack is exactly the per-layer calls
     K2 = dev(np.stack(K), torch.bfloat16)
     V2 = dev(np.stack(V), torch.bfloat16)
     F.rope_shift(cfg, rope, K2, p.T * p.kv_dim, L, p.T, offs)
