@@ -187,6 +187,9 @@ def test_8bit_calls_argument_errors(cblib):
     many = (ctypes.c_int32 * 258)(*range(258))
     assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 300, many,
               257, 1, None) == 5
+    # nothing to expand: no device access at all
+    assert kv(ctypes.byref(cfg), None, FAKE, FAKE, FAKE, FAKE, 1, 0, 0, FAKE, FAKE, 0, 100, offs, 2, 0, None) == 0
+    assert kv(ctypes.byref(cfg), None, FAKE, FAKE, FAKE, FAKE, 0, 0, 100, FAKE, FAKE, 0, 100, offs, 2, 0, None) == 0
     # the 8-bit stack needs all four sources
     ks = (ctypes.c_int32 * 2)(10, 10)
     Wl = (F.LayerWeights * 2)(F.LayerWeights(*([FAKE] * 9)), F.LayerWeights(*([FAKE] * 9)))

@@ -141,3 +141,32 @@ def test_llama8b_layer_fp8_full_size_sampled():
     e = rel_err(got["y"][rows], y)
     print(f"\nllama8b_layer 8-bit: sampled output max-rel error {e:.3g}")
     assert e < TOL
+
+
+def test_fp8_degenerate_cases():
+    """k = 0 (only the query is recomputed), k >= candidates (every row) and a
+    query-only input, on the 8-bit layer."""
+    need_gpu()
+    p = LONG
+    case = single_layer_case(p, 3, prepass_inputs=False)
+    cfg = F.config_of(p)
+    w8 = fp8.quantize_layer(case["w"])
+    lin = fp8.projector(w8, "bf16")
+    L = _device_weights(cfg, case["w"], w8)
+    rope = F.DeviceRope(cfg, p.T)
+    ws = F.workspace_fp8(cfg, p.T, p.T)
+    T, n_ctx, L0 = p.T, p.n_ctx, case["L0"]
+    hidden = dev(case["hidden"], torch.bfloat16)
+    s_all = np.arange(L0, T)
+    for k in (0, n_ctx - L0, n_ctx):
+        got = _blend(cfg, p, L, rope, ws, case["k"], case["v"], s_all, hidden, L0, k)
+        want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_all, case["hidden"][s_all], k,
+                                 store="bf16", keep=None if k else np.zeros(0, np.int64), lin=lin)
+        assert np.array_equal(got["s_out"], s_all if k else np.arange(n_ctx, T))
+        _check_blend(p, case, got, want, s_all)
+    q_only = np.arange(n_ctx, T)
+    got = _blend(cfg, p, L, rope, ws, case["k"], case["v"], q_only, hidden, L0, 5)
+    want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, q_only, case["hidden"][q_only], 5,
+                             store="bf16", lin=lin)
+    assert np.array_equal(got["s_out"], q_only)
+    _check_blend(p, case, got, want, q_only)
