@@ -86,7 +86,10 @@ typedef struct {
 } cb_layer_config;
 
 /* Device pointers to one layer's weights (layouts above).  attn_norm and
- * mlp_norm are fp32 [d_model]. */
+ * mlp_norm are fp32 [d_model].  w_gateup_packed is optional (NULL = unused):
+ * W_gate and W_up repacked once by cb_pack_gateup, which the bf16 gate/up
+ * projection then streams instead of w_gate and w_up (same results, bit for
+ * bit). */
 typedef struct {
   const void* attn_norm;
   const void* w_q;
@@ -97,6 +100,7 @@ typedef struct {
   const void* w_gate;
   const void* w_up;
   const void* w_down;
+  const void* w_gateup_packed;
 } cb_layer_weights;
 
 /* Device RoPE table: cos[p][hd/2], sin[p][hd/2] fp32 for p = 0 .. n_pos-1,
@@ -131,6 +135,18 @@ int32_t cb_num_selected(int32_t r_e4, int32_t n_ctx, int32_t n_cand);
  * never grows from one layer to the next. */
 cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, int32_t r_last_e4,
                              int32_t n_ctx, int32_t n_cand, int32_t* k_out);
+
+/* One-time weight repack (a model-load step, not part of a request).  The
+ * gate/up projection streams 256-row tiles (128 gate rows, then the same 128
+ * up rows) in 32-element K steps; cb_pack_gateup stores W_gate and W_up (bf16
+ * device [ffn][d] each) in exactly that order, tile by tile and step by step,
+ * each (tile, step) block of 256 rows x 64 bytes contiguous, rows past ffn
+ * and K past d zero, so that every load of the kernel reads contiguous
+ * memory.  packed: device, cb_pack_gateup_size(cfg) bytes, 16-byte aligned.
+ * CB_ERR_UNSUPPORTED for fp32 configs (the fp32 path does not use it). */
+size_t cb_pack_gateup_size(const cb_layer_config* cfg);
+cb_status cb_pack_gateup(const cb_layer_config* cfg, const void* w_gate, const void* w_up,
+                         void* packed, void* stream);
 
 /* Bytes of device workspace needed by cb_blend_layer with up to m_max input
  * rows and by cb_full_prefill_layer with T <= m_max rows, and by

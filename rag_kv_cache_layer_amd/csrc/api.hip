@@ -192,6 +192,7 @@ cb_status check_weights(const cb_layer_weights* w) {
   const void* p[9] = {w->attn_norm, w->w_q, w->w_k, w->w_v, w->w_o, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
   for (const void* x : p)
     if (!x || !aligned16(x)) return CB_ERR_ARG;
+  if (w->w_gateup_packed && !aligned16(w->w_gateup_packed)) return CB_ERR_ARG;
   return CB_OK;
 }
 
@@ -324,6 +325,7 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   gu.B.p1 = w.w_up;
   gu.B.p2 = w.w_up;
   gu.B.n_feat = D.F;
+  gu.B.packed = dt == CB_BF16 ? w.w_gateup_packed : nullptr;
   gu.epi.kind = EPI_SWIGLU;
   gu.epi.out = at<void>(ws, L.u);
   gu.epi.ld_out = D.F;
@@ -755,6 +757,20 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   if (m_in == 0) return CB_OK;
   return cb::blend_run(*cfg, *w, *rope, k_cache, v_cache, T, n_ctx, first_chunk_len, s_in, m_in, hidden_in, in_rows,
                        k_out, hidden_out, dev_out, s_out, ws, (hipStream_t)stream);
+}
+
+extern "C" size_t cb_pack_gateup_size(const cb_layer_config* cfg) {
+  if (check_cfg(cfg) != CB_OK || cfg->dtype != CB_BF16) return 0;
+  return pack_gateup_bytes(cfg->ffn_dim, cfg->d_model);
+}
+
+extern "C" cb_status cb_pack_gateup(const cb_layer_config* cfg, const void* w_gate, const void* w_up, void* packed,
+                                    void* stream) {
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != CB_BF16) return CB_ERR_UNSUPPORTED;
+  if (!w_gate || !w_up || !packed || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(packed)) return CB_ERR_ARG;
+  return hip_status(launch_pack_gateup(w_gate, w_up, cfg->ffn_dim, cfg->d_model, packed, (hipStream_t)stream));
 }
 
 extern "C" size_t cb_workspace_size_fp8(const cb_layer_config* cfg, int32_t T, int32_t m_max) {

@@ -211,7 +211,21 @@ struct BOperand {
   const void* p2;
   int n1, n2;
   int n_feat;
+  // mode 1 only, optional: the pair already in the large kernel's streaming
+  // order (see launch_pack_gateup); p0/p1 are then not read
+  const void* packed;
 };
+// The gate/up operand in the order the 256-wide gated kernel streams it: for
+// each tile of kGateupTile/2 features and each kGateupStep-element K step,
+// the tile's gate rows then the same up rows, kGateupStep elements each, as
+// one contiguous block; rows past n_feat and K past K are zero.
+constexpr int kGateupTile = 256, kGateupStep = 32;
+__host__ __device__ inline size_t pack_gateup_bytes(int n_feat, int K) {
+  const size_t tiles = (size_t)(n_feat + kGateupTile / 2 - 1) / (kGateupTile / 2);
+  const size_t nk = (size_t)(K + kGateupStep - 1) / kGateupStep;
+  return tiles * nk * kGateupTile * kGateupStep * 2;
+}
+hipError_t launch_pack_gateup(const void* w_gate, const void* w_up, int n_feat, int K, void* packed, hipStream_t s);
 
 enum EpiKind { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_STORE = 3 };
 

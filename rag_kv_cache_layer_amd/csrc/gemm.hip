@@ -416,6 +416,7 @@ constexpr int kLFA = kLWTM / 16, kLFB = kLWTN / 16;  // MFMA blocks per wave
 constexpr int kLStage = (LBM + LBN) * LBK * 2;       // 30 or 32 KB
 static_assert(LNS >= 2 && LNS <= 5 && LNS * kLStage <= 160 * 1024, "ring depth");
 constexpr int kLSmem = LNS * kLStage > 128 * LCLD * 4 ? LNS * kLStage : 128 * LCLD * 4;
+static_assert(LBK == kGateupStep, "the packed gate/up layout follows the large kernel's K step");
 constexpr int kLBlocksA = LBM / 16, kLBlocks = (LBM + LBN) / 16;   // 1 KB blocks per stage
 constexpr int kLBPW = (kLBlocks + kLW - 1) / kLW;   // blocks per wave (at most)
 static_assert(kLBPW <= 8 && kLFA % kLBPW == 0, "blocks are issued between MFMA rows");
@@ -465,10 +466,19 @@ __global__ __launch_bounds__(kLNT, 1) void gemm_bf16_big_kernel(GemmArgs g, int 
   __amdgpu_buffer_rsrc_t rs[kLBPW];
   uint32_t off[kLBPW];
   int dst[kLBPW];
+  // packed gate/up operand: block (tile tn, step s) starts at
+  // (tn * nk + s) * LBN * 64 bytes; off[] then holds the lane's byte offset
+  // inside the block
+  const bool packed = LBN == kGateupTile && g.B.mode == 1 && g.B.packed != nullptr;
 #pragma unroll
   for (int j = 0; j < kLBPW; ++j) {
     const int blk = min(w + kLW * j, kLBlocks - 1);
-    if (blk < kLBlocksA) {
+    if (blk >= kLBlocksA && packed) {
+      const int r0 = (blk - kLBlocksA) * 16;
+      rs[j] = make_rsrc(g.B.packed, (uint32_t)pack_gateup_bytes(g.B.n_feat, K));
+      off[j] = (uint32_t)((r0 + rl) * 64 + lcol * 2);
+      dst[j] = blk * 1024;
+    } else if (blk < kLBlocksA) {
       const int row = blk * 16 + rl;
       rs[j] = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
       off[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
@@ -495,8 +505,13 @@ __global__ __launch_bounds__(kLNT, 1) void gemm_bf16_big_kernel(GemmArgs g, int 
   }
   auto issue_group = [&](int stage, int k0, int j) {
     if (j >= nbw) return;
-    const int kk = k0 + lcol;
-    const uint32_t o = (kk < K && off[j] != kOOB) ? off[j] + kk * 2 : kOOB;
+    uint32_t o;
+    if (packed && w + kLW * j >= kLBlocksA) {
+      o = (uint32_t)((tn * nk + k0 / LBK) * (LBN * 64)) + off[j];
+    } else {
+      const int kk = k0 + lcol;
+      o = (kk < K && off[j] != kOOB) ? off[j] + kk * 2 : kOOB;
+    }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kLStage + dst[j]), 16, o, 0, 0, 0);
   };
   auto issue = [&](int stage, int k0) {
@@ -768,6 +783,40 @@ int gemm_splits(int dtype, int n_tiles, int K) {
   int s = 1;
   while (s < 4 && n_tiles * s < CB_SPLIT_TILES && K / (2 * s) >= 1024) s *= 2;
   return s;
+}
+
+namespace {
+
+// one thread per 16-byte chunk of the packed operand
+__global__ __launch_bounds__(256) void pack_gateup_kernel(const bf16_t* __restrict__ gate,
+                                                          const bf16_t* __restrict__ up, int n_feat, int K, int nk,
+                                                          int64_t n_chunks, u32x4_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_chunks) return;
+  const int c = (int)(q & 3);                                  // 16-byte chunk of a 64-byte row step
+  const int r = (int)((q >> 2) % kGateupTile);                 // row of the tile
+  const int64_t ts = (q >> 2) / kGateupTile;                   // tile * nk + step
+  const int step = (int)(ts % nk), tile = (int)(ts / nk);
+  const int f = tile * (kGateupTile / 2) + (r % (kGateupTile / 2));
+  const int col = step * kGateupStep + c * 8;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (f < n_feat && col < K) {
+    const bf16_t* src = (r < kGateupTile / 2 ? gate : up) + (int64_t)f * K + col;
+    v = *reinterpret_cast<const u32x4_t*>(src);
+  }
+  out[q] = v;
+}
+
+}  // namespace
+
+hipError_t launch_pack_gateup(const void* w_gate, const void* w_up, int n_feat, int K, void* packed, hipStream_t s) {
+  const int64_t n_chunks = (int64_t)(pack_gateup_bytes(n_feat, K) / 16);
+  if (n_chunks == 0) return hipSuccess;
+  const int nk = (K + kGateupStep - 1) / kGateupStep;
+  LaunchScope ls("pack_gateup", s);
+  pack_gateup_kernel<<<(unsigned)((n_chunks + 255) / 256), 256, 0, s>>>((const bf16_t*)w_gate, (const bf16_t*)w_up,
+                                                                       n_feat, K, nk, n_chunks, (u32x4_t*)packed);
+  return hipGetLastError();
 }
 
 hipError_t launch_epilogue_only(const GemmArgs& g0, hipStream_t s) {

@@ -44,7 +44,8 @@ class LayerConfig(ctypes.Structure):
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up", "w_down")]
+                ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up", "w_down",
+                 "w_gateup_packed")]
 
 
 class LayerWeightsFp8(ctypes.Structure):
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
                                      I32P, P, SZ, P, P]),
         "cb_kv_from_fp8": (I32, [CFG, R, P, P, P, P, I32, I32, I32, P, P, I64, I32, I32P, I32, I32, P]),
         "cb_workspace_size_fp8": (SZ, [CFG, I32, I32]),
+        "cb_pack_gateup_size": (SZ, [CFG]),
+        "cb_pack_gateup": (I32, [CFG, P, P, P, P]),
         "cb_blend_layer_fp8": (I32, [CFG, ctypes.POINTER(LayerWeightsFp8), R, P, P, I32, I32, I32, P, I32, P, P, I32,
                                      P, P, P, I32P, P, SZ, P]),
     }
@@ -270,6 +273,22 @@ class DeviceLayer:
         self.struct = LayerWeights(*[self.t[n].data_ptr() for n in
                                      ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up",
                                       "w_down")])
+        self.cfg = cfg
+
+    def pack_gateup(self, stream=None) -> "DeviceLayer":
+        """cb_pack_gateup: repack W_gate and W_up once into the gate/up
+        kernel's streaming order; the layer's calls then read the packed copy
+        (same results, bit for bit).  Returns self."""
+        torch = _torch()
+        n = int(lib().cb_pack_gateup_size(ctypes.byref(self.cfg)))
+        if n == 0:
+            raise CacheBlendError(5, "cb_pack_gateup_size")
+        self.t["w_gateup_packed"] = torch.empty(n, dtype=torch.uint8, device=self.t["w_gate"].device)
+        _check(lib().cb_pack_gateup(ctypes.byref(self.cfg), _dptr(self.t["w_gate"], "w_gate"),
+                                    _dptr(self.t["w_up"], "w_up"), _dptr(self.t["w_gateup_packed"], "packed"),
+                                    _stream(stream)), "cb_pack_gateup")
+        self.struct.w_gateup_packed = self.t["w_gateup_packed"].data_ptr()
+        return self
 
 
 class DeviceLayerFp8:

@@ -202,3 +202,14 @@ def test_validate_switch(cblib):
     assert F.set_validate(True) is False
     assert F.set_validate(False) is True
     assert F.set_validate(False) is False
+
+
+def test_pack_gateup_argument_errors(cblib):
+    L, cfg = cblib, _cfg()
+    assert int(L.cb_pack_gateup_size(ctypes.byref(cfg))) == 8 * 16 * 256 * 64   # 1024/128 tiles x 512/32 steps
+    assert int(L.cb_pack_gateup_size(ctypes.byref(_cfg(dtype="f32")))) == 0
+    assert L.cb_pack_gateup(ctypes.byref(_cfg(dtype="f32")), FAKE, FAKE, FAKE, None) == 5
+    assert L.cb_pack_gateup(ctypes.byref(cfg), None, FAKE, FAKE, None) == 1
+    assert L.cb_pack_gateup(ctypes.byref(cfg), FAKE, FAKE, FAKE + 4, None) == 1
+    w = F.LayerWeights(*([FAKE] * 9 + [FAKE + 2]))                               # misaligned packed copy
+    assert _blend(L, cfg, w=w)[0] == 1
