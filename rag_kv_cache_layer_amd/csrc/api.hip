@@ -686,7 +686,11 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
     st = hip_status(launch_gemm(dt, g, s));
   }
   if (st) return st;
-  // 3. deviation sums + top-k + query rows
+  // 3. deviation sums + top-k + query rows.  A layer that keeps every
+  // recomputed row (k_out >= candidates: the blend call at a fixed ratio)
+  // needs no ranking; on the bf16 path the attention kernel then writes the
+  // deviation sums and the kept ids, and the kept rows are the input rows.
+  const bool keep_all = dt == CB_BF16 && k_out >= n_cand;
   SelectArgs sa{};
   sa.dev_part = at<float>(ws, L.devp);
   sa.n_parts = D.n_k_tiles();
@@ -698,13 +702,24 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   sa.ids_in = s_in;
   sa.sel = at<int>(ws, L.sel);
   sa.ids_out = s_out;
-  st = hip_status(launch_select(sa, s));
-  if (st) return st;
+  if (!keep_all) {
+    st = hip_status(launch_select(sa, s));
+    if (st) return st;
+  }
   // 4. attention of the kept rows over the blended cache
   AttnArgs aa{};
   aa.Q = at<void>(ws, L.q);
-  aa.qmap = at<int>(ws, L.sel);
-  aa.qpos = s_out;
+  aa.qmap = keep_all ? nullptr : at<int>(ws, L.sel);
+  aa.qpos = keep_all ? s_in : s_out;
+  if (keep_all) {
+    aa.fin_ids_in = s_in;
+    aa.fin_ids_out = s_out;
+    aa.fin_dev_part = sa.dev_part;
+    aa.fin_dev = sa.dev;
+    aa.fin_n_parts = sa.n_parts;
+    aa.fin_ld_part = sa.ld_part;
+    aa.fin_n_cand = n_cand;
+  }
   aa.K = k_cache;
   aa.V = v_cache;
   aa.O = at<void>(ws, L.o);
@@ -719,8 +734,8 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
   // 5. O projection, MLP
-  return layer_tail(c, w, L, ws, m_out, hidden_in, n_src, at<int>(ws, L.sel), in_rows, hidden_out, s, w8,
-                    w8 ? &F8 : nullptr);
+  return layer_tail(c, w, L, ws, m_out, hidden_in, n_src, keep_all ? nullptr : at<int>(ws, L.sel), in_rows,
+                    hidden_out, s, w8, w8 ? &F8 : nullptr);
 }
 
 }  // namespace

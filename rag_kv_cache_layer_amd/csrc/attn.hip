@@ -147,6 +147,20 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = kvh * G + w;
   const int q = lane & 15, gp = lane >> 4;
+  if (a.fin_ids_out && kvh == 0 && split == 0 && w == 0) {
+    // selection outputs of a layer that keeps every row (one wave per row tile)
+    for (int i = ti.r0 + lane; i < ti.r1; i += 64) {
+      a.fin_ids_out[i] = a.fin_ids_in[i];
+      float sdev;
+      if (i < a.fin_n_cand) {
+        sdev = 0.f;
+        for (int t = 0; t < a.fin_n_parts; ++t) sdev += a.fin_dev_part[(int64_t)t * a.fin_ld_part + i];
+      } else {
+        sdev = __builtin_nanf("");
+      }
+      a.fin_dev[i] = sdev;
+    }
+  }
 
   int pos[2];
   bool valid[2];

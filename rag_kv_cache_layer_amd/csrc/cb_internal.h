@@ -317,6 +317,15 @@ struct AttnArgs {
   float* o_part;          // [T / key_split][m][n_q][hd] unnormalised partials (key_split > 0)
   float* ml_part;         // [T / key_split][m][n_q][2] running max (log2 units) and sum
   ReqTable req;           // several requests: row ranges, row tiles, K/V and T per request (T = max)
+  // When a layer keeps every recomputed row, no selection kernel runs and the
+  // bf16 attention writes its outputs instead (fin_ids_out != NULL):
+  // fin_ids_out[i] = fin_ids_in[i], fin_dev[i] = the sum of the fin_n_parts
+  // deviation partials in order (NaN for i >= fin_n_cand), i < m.
+  const int* fin_ids_in;
+  int* fin_ids_out;
+  const float* fin_dev_part;
+  float* fin_dev;
+  int fin_n_parts, fin_ld_part, fin_n_cand;
 };
 // Key-split length used for m query rows over T keys (0 = none): a multiple
 // of 64, at least 512; chosen from the row, head and key counts only.

@@ -176,6 +176,31 @@ def test_blend_degenerate_cases(p):
     _check_blend(p, case, got, want, q_only)
 
 
+@pytest.mark.parametrize("p", [MED64, LONG], ids=["bf16_hd64", "bf16_long"])
+def test_keep_all_matches_ranking_path(p):
+    """A layer that keeps every recomputed row (k_out >= candidates) runs no
+    ranking kernel: its deviations and kept ids come from the attention
+    kernel.  They equal, bit for bit, what the ranking path gives on the same
+    inputs, and its K/V equal the ranking path's and its outputs agree on the common rows."""
+    need_gpu()
+    case = single_layer_case(p, 5)
+    g = Gpu(p, case)
+    T, n_ctx, L0 = p.T, p.n_ctx, case["L0"]
+    s_in = np.arange(L0, T)
+    n_cand = n_ctx - L0
+    keep = g.blend(case["k"], case["v"], s_in, case["hidden"], s_in, n_cand)     # keeps every row
+    rank = g.blend(case["k"], case["v"], s_in, case["hidden"], s_in, n_cand - 1)  # ranks, drops one
+    assert np.array_equal(keep["s_out"], s_in)
+    assert np.array_equal(keep["dev"][:n_cand], rank["dev"][:n_cand])
+    assert np.all(np.isnan(keep["dev"][n_cand:]))
+    assert np.array_equal(keep["k"], rank["k"]) and np.array_equal(keep["v"], rank["v"])
+    # the rows both calls keep have the same layer output (up to the rounding
+    # of the attention key split, which follows the kept-row count)
+    pos = {int(t): i for i, t in enumerate(keep["s_out"])}
+    idx = [pos[int(t)] for t in rank["s_out"]]
+    assert rel_err(keep["y"][idx], rank["y"]) < tol_of(p)
+
+
 def test_r1_blend_equals_full_prefill_gpu():
     """r = 1 on a layer whose cache and inputs come from full prefill gives
     full prefill back (section 4.2: r% of the tokens -> 100% is full prefill)."""
