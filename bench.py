@@ -240,6 +240,7 @@ def main():
         torch.cuda.synchronize()
         extra["full_prefill_ms"] = round((time.perf_counter() - t0) * 100, 4)
         extra["shift_stack"] = shift_stack_measure()
+        extra["kdev_cold"] = kdev_cold_measure()
         extra["kv_expand_stack"] = kv_expand_measure()
 
     if args.batch > 1:
@@ -403,6 +404,46 @@ def shift_stack_measure(reps=6):
     return {"layers": L, "bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "copy_same_bytes_gbs": round(nbytes / (cms * 1e-3) / 1e9, 1)}
+
+
+def kdev_cold_measure(reps=6):
+    """The standalone K deviation of cb_select_hkvd (k_new given) over the
+    candidates of the 8B layer with 32 chunks x 512 + 64 tokens (15872 rows of
+    8 KV heads x 128): each call reads the new K rows and the cached K rows
+    (65 MB), rotating over four sets of buffers (260 MB) so that no call finds
+    its data in the 256 MB Infinity Cache.  The kernel's own time comes from
+    the library's per-launch events ("kdev"); the top-k of the same call is
+    reported beside it."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    from rag_kv_cache_layer_amd import synth
+    p = synth.sweep_preset(32, 1500)
+    cfg = F.config_of(p)
+    T, kvd = p.T, p.kv_dim
+    L0 = 512
+    n = p.n_ctx - L0
+    k = F.num_selected(1500, p.n_ctx, n)
+    rows = torch.arange(L0, L0 + n, dtype=torch.int32, device="cuda")
+    sets = [(torch.randn((n, kvd), device="cuda").to(torch.bfloat16),
+             torch.randn((T, kvd), device="cuda").to(torch.bfloat16)) for _ in range(4)]
+    dv = torch.empty(n, dtype=torch.float32, device="cuda")
+    so = torch.empty(k, dtype=torch.int32, device="cuda")
+    ws = F.workspace(cfg, T, T)
+    F.select_hkvd(cfg, sets[0][0], sets[0][1], T, rows, n, k, dv, so, ws)
+    torch.cuda.synchronize()
+    F.profile_begin()
+    for i in range(reps):
+        F.select_hkvd(cfg, sets[(i + 1) % 4][0], sets[(i + 1) % 4][1], T, rows, n, k, dv, so, ws)
+    torch.cuda.synchronize()
+    st = F.profile_end()
+    kd = st["kdev"]
+    ms = kd["total_ms"] / kd["launches"]
+    nbytes = 2 * n * kvd * 2
+    out = {"rows": n, "bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if "select_topk" in st:
+        out["topk_ms"] = round(st["select_topk"]["total_ms"] / st["select_topk"]["launches"], 4)
+    return out
 
 
 def sweep_measure(seed, steps):

@@ -202,7 +202,25 @@ __global__ __launch_bounds__(256) void kdev_kernel(const T* __restrict__ k_new, 
   const int r = rows ? rows[i] : i;
   float s = 0.f;
   if (r >= 0 && r < T_rows) {
-    for (int c = lane * 8; c < kv_dim; c += 64 * 8) {
+    // two 512-element steps per iteration: all four 16-byte loads are issued
+    // before the arithmetic (same accumulation order as one step at a time)
+    int c = lane * 8;
+    for (; c + 512 < kv_dim; c += 2 * 512) {
+      float x[2][8], y[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        load8(k_new + (int64_t)i * kv_dim + c + u * 512, x[u]);
+        load8(k_ref + (int64_t)r * kv_dim + c + u * 512, y[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float d = x[u][j] - y[u][j];
+          s += d * d;
+        }
+    }
+    for (; c < kv_dim; c += 512) {
       float x[8], y[8];
       load8(k_new + (int64_t)i * kv_dim + c, x);
       load8(k_ref + (int64_t)r * kv_dim + c, y);
