@@ -113,6 +113,13 @@ struct ReqTable {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// SwiGLU gate: silu(g) = g / (1 + e^-g), with the hardware base-2 exponent
+// and reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each); e^-g overflowing to
+// infinity gives -0 for large negative g.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
 // Buffer resource over `bytes` bytes at p (gfx9 layout: raw buffer, no
 // stride); loads past `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {

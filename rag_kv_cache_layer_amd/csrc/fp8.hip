@@ -342,7 +342,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int
         const float* gp = Cs + r * QLCLD + c;
         float o[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) o[x] = (gp[x] / (1.0f + expf(-gp[x]))) * gp[x + QLN / 2];
+        for (int x = 0; x < 8; ++x) o[x] = silu(gp[x]) * gp[x + QLN / 2];
         bf16_t* dst = (bf16_t*)g.C + (int64_t)row * g.ldc + f;
         if (vec && f + 8 <= GF) {
           store8(dst, o);

@@ -141,7 +141,7 @@ template <typename T>
 __device__ void epi_swiglu(const EpiParams& e, int gm, int f, const float g[8], const float u[8]) {
   float o[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = (g[j] / (1.0f + expf(-g[j]))) * u[j];
+  for (int j = 0; j < 8; ++j) o[j] = silu(g[j]) * u[j];
   store8((T*)e.out + (int64_t)gm * e.ld_out + f, o);
 }
 
