@@ -59,6 +59,10 @@ def parse():
                          "tokens at r = 0.05, 0.10, 0.15, 0.30, 1.0")
     ap.add_argument("--llama70b", action="store_true",
                     help="also time the blend call of one Llama-70B-shaped layer (8 x 500 + 32 tokens, r=0.15)")
+    ap.add_argument("--cpu-extra", action="store_true",
+                    help="also time the CPU oracle on the other workloads: the tiny fp32 layer (1 thread and all), "
+                         "full prefill of the 8B layer, the 4-chunk sweep layer at r = 0.15 and 1, and spot layers "
+                         "of the 32-layer 8B and 80-layer 70B stacks (scaled by the layer count, an estimate)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 512 MiB device-to-device copy first (a known-size reference "
                          "for the HBM byte counters)")
@@ -331,6 +335,9 @@ def main():
     if not args.no_cpu:
         log("timing the CPU oracle")
         cpu = cpu_baseline(p, seed, k, args.cpu_seconds)
+        if args.cpu_extra:
+            log("timing the CPU oracle on the other workloads")
+            cpu["extra"] = cpu_extra_measure(seed)
 
     out = {
         "metric": "blended-context tokens/s at r=0.15 (Llama-8B-shaped layer)",
@@ -852,6 +859,86 @@ def cpu_baseline(p, seed, k, budget_s):
     return {"value": round(T / t, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} oracle blend calls (numpy fp32, {threads} BLAS threads) of the same layer "
                       f"and shapes, median {t * 1e3:.0f} ms"}
+
+
+def cpu_extra_measure(seed, reps=3):
+    """The oracle (numpy fp32, the host's BLAS threads unless stated) on the
+    other workloads, median of `reps` calls (one call for the large layers):
+    blend call = selective recompute of k candidates + the query at ratio r;
+    full prefill = the same layer over all T rows.  Stack figures are one
+    layer's time times the layer count (an estimate, labelled so)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import blend, layer
+    from rag_kv_cache_layer_amd import synth
+
+    def med(f, n):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    def case(p, k, n_rep):
+        T, n_ctx = p.T, p.n_ctx
+        L0 = p.chunk_lens[0]
+        w = synth.layer_weights(p, seed, 0)
+        K = synth.random_normal(p, seed, (T, p.n_kv_heads, p.head_dim), tag_layer=11)
+        V = synth.random_normal(p, seed, (T, p.n_kv_heads, p.head_dim), tag_layer=12)
+        x = synth.random_normal(p, seed, (T, p.d_model), tag_layer=13)
+        S = np.concatenate([synth.random_subset(p, seed, L0, n_ctx, min(k, n_ctx - L0)),
+                            np.arange(n_ctx, T)]).astype(np.int64)
+        st = "bf16" if p.dtype == "bf16" else None
+        return (lambda: blend.blend_layer(w, p, K, V, n_ctx, S, x[S], k, store=st),
+                lambda: layer.full_prefill(w, x, p, 0, store=st))
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    out = {"threads": threads}
+    tiny = synth.PRESETS["tiny_f32"]
+    kt = blend.num_selected(tiny.r_e4, tiny.n_ctx, tiny.n_ctx - tiny.chunk_lens[0])
+    bl, fp = case(tiny, kt, 1)
+    out["tiny_f32"] = {"T": tiny.T, "k": kt, "blend_ms": round(med(bl, 7) * 1e3, 3),
+                       "full_prefill_ms": round(med(fp, 7) * 1e3, 3)}
+    with threadpool_limits(1):
+        out["tiny_f32"]["blend_ms_1thread"] = round(med(bl, 7) * 1e3, 3)
+        out["tiny_f32"]["full_prefill_ms_1thread"] = round(med(fp, 7) * 1e3, 3)
+    log("cpu extra: tiny done")
+    p8 = synth.PRESETS["llama8b_layer"]
+    k8 = blend.num_selected(p8.r_e4, p8.n_ctx, p8.n_ctx - p8.chunk_lens[0])
+    _, fp = case(p8, k8, 1)
+    out["llama8b_layer"] = {"T": p8.T, "full_prefill_ms": round(med(fp, 1) * 1e3, 1)}
+    log("cpu extra: 8B full prefill done")
+    sw = synth.sweep_preset(4, 1500)
+    res = {"T": sw.T}
+    for r_e4 in (1500, 10000):
+        k = blend.num_selected(r_e4, sw.n_ctx, sw.n_ctx - sw.chunk_lens[0])
+        bl, fp = case(sw, k, reps)
+        res[f"blend_ms_r{r_e4 / 1e4:g}"] = round(med(bl, reps) * 1e3, 1)
+    res["full_prefill_ms"] = round(med(fp, 1) * 1e3, 1)
+    out["sweep_4_chunks"] = res
+    log("cpu extra: sweep done")
+    st = synth.PRESETS["llama8b_stack"]
+    ks = blend.filter_schedule(st.n_layers, st.r_e4, st.r_last_e4, st.n_ctx, st.n_ctx - st.chunk_lens[0])
+    k_mean = int(round(float(np.mean(ks))))
+    bl, _ = case(st, k_mean, 1)
+    t = med(bl, 1)
+    out["llama8b_stack"] = {"T": st.T, "layers": st.n_layers, "k_mean": k_mean, "layer_ms": round(t * 1e3, 1),
+                            "stack_ms_estimate": round(t * 1e3 * st.n_layers, 0)}
+    log("cpu extra: 8B stack spot layer done")
+    p70 = synth.PRESETS["llama70b_stack"]
+    k70 = blend.num_selected(p70.r_e4, p70.n_ctx, p70.n_ctx - p70.chunk_lens[0])
+    bl, fp = case(p70, k70, 1)
+    log("cpu extra: 70B inputs ready")
+    tb = med(bl, 1)
+    log("cpu extra: 70B blend layer done")
+    tf = med(fp, 1)
+    out["llama70b_stack"] = {"T": p70.T, "layers": p70.n_layers, "k": k70, "blend_layer_ms": round(tb * 1e3, 1),
+                             "full_prefill_layer_ms": round(tf * 1e3, 1),
+                             "blend_stack_ms_estimate": round(tb * 1e3 * p70.n_layers, 0),
+                             "full_prefill_stack_ms_estimate": round(tf * 1e3 * p70.n_layers, 0)}
+    log("cpu extra: 70B spot layers done")
+    return out
 
 
 if __name__ == "__main__":
