@@ -399,6 +399,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
 // always in bounds; values read for a tile that was not split are dropped).
 template <int HD>
 constexpr int merge_heads() { return 256 / (HD / 4); }
+constexpr int kMergeRegs = 8;   // splits a merge thread holds in registers at once
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
@@ -429,17 +430,44 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   if (head < a.n_q) {
     const int64_t stride = (int64_t)a.m * a.n_q;   // slots per split
     const int64_t slot0 = (int64_t)i * a.n_q + head;
-    float mx = -INFINITY;
+    if (ns <= kMergeRegs) {
+      // every split's (max, sum) and output slice loaded at once (one memory
+      // round trip), then the same arithmetic in the same order as below
+      float2 ml[kMergeRegs];
+      float4 o[kMergeRegs];
+#pragma unroll
+      for (int sp = 0; sp < kMergeRegs; ++sp) {
+        if (sp < ns) {
+          const int64_t slot = slot0 + sp * stride;
+          ml[sp] = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
+          o[sp] = *reinterpret_cast<const float4*>(a.o_part + slot * HD + c);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < kMergeRegs; ++sp)
+        if (sp < ns) mx = fmaxf(mx, ml[sp].x);
+#pragma unroll
+      for (int sp = 0; sp < kMergeRegs; ++sp) {
+        if (sp < ns) {
+          const float wgt = exp2f(ml[sp].x - mx);
+          den += wgt * ml[sp].y;
+          num.x += wgt * o[sp].x; num.y += wgt * o[sp].y; num.z += wgt * o[sp].z; num.w += wgt * o[sp].w;
+        }
+      }
+    } else {
+      float mx = -INFINITY;
 #pragma unroll 8
-    for (int sp = 0; sp < ns; ++sp) mx = fmaxf(mx, a.ml_part[(slot0 + sp * stride) * 2]);
+      for (int sp = 0; sp < ns; ++sp) mx = fmaxf(mx, a.ml_part[(slot0 + sp * stride) * 2]);
 #pragma unroll 8
-    for (int sp = 0; sp < ns; ++sp) {
-      const int64_t slot = slot0 + sp * stride;
-      const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
-      const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + c);
-      const float wgt = exp2f(ml.x - mx);
-      den += wgt * ml.y;
-      num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;
+      for (int sp = 0; sp < ns; ++sp) {
+        const int64_t slot = slot0 + sp * stride;
+        const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
+        const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + c);
+        const float wgt = exp2f(ml.x - mx);
+        den += wgt * ml.y;
+        num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;
+      }
     }
   }
   __syncthreads();
