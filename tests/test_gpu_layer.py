@@ -201,6 +201,27 @@ def test_keep_all_matches_ranking_path(p):
     assert rel_err(keep["y"][idx], rank["y"]) < tol_of(p)
 
 
+def test_swiglu_gate_extremes():
+    """Gate pre-activations far outside [-80, 80] (W_gate scaled 200x): the
+    SwiGLU epilogue's silu (hardware exp2 and reciprocal) saturates to 0 and
+    to g exactly where the oracle's plain g / (1 + e^-g) does."""
+    need_gpu()
+    p = MED64
+    case = single_layer_case(p, 6)
+    case["w"] = dict(case["w"])
+    case["w"]["w_gate"] = synth.round_to(case["w"]["w_gate"] * np.float32(200.0), "bf16")
+    g = Gpu(p, case)
+    st = store_of(p)
+    T, n_ctx, L0 = p.T, p.n_ctx, case["L0"]
+    s_in = np.arange(L0, T)
+    k = n_ctx - L0
+    got = g.blend(case["k"], case["v"], s_in, case["hidden"], s_in, k)
+    with np.errstate(over="ignore"):
+        want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_in, case["hidden"][s_in], k, store=st)
+    assert np.all(np.isfinite(got["y"]))
+    _check_blend(p, case, got, want, s_in)
+
+
 def test_r1_blend_equals_full_prefill_gpu():
     """r = 1 on a layer whose cache and inputs come from full prefill gives
     full prefill back (section 4.2: r% of the tokens -> 100% is full prefill)."""
