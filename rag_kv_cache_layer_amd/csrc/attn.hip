@@ -37,6 +37,7 @@
 // fp32 path: one wave per (row, head); scores in LDS, two-pass softmax.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "cb_internal.h"
 
@@ -62,6 +63,14 @@ constexpr int kStages = CB_ATTN_NS;
 static_assert(kStages >= 2 && kStages <= 4, "ring depth");
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+// vector instructions placed between the matrix instructions of the two
+// overlapped phases of a key tile (scores / mask-max, P V / probabilities)
+#ifndef CB_ATTN_SG_B
+#define CB_ATTN_SG_B 3
+#endif
+#ifndef CB_ATTN_SG_E
+#define CB_ATTN_SG_E 8
+#endif
 #ifndef CB_ATTN_SPLIT
 #define CB_ATTN_SPLIT 512
 #endif
@@ -264,99 +273,135 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
       const char* sk = smem + u * kStage;
       const char* sv = sk + kTile;
 
-      // S^T[key][query]: lane holds keys t0+16kb+4gp+v of queries q (b=0) and 16+q (b=1)
-      f32x4_t s[2][KB];
+      // S^T[key][query]: lane holds keys t0+16kb+4gp+v of queries q (b=0) and 16+q (b=1).
+      // The tile is worked in two halves of 32 keys with an explicit
+      // instruction schedule, so that the matrix cores run one half while the
+      // vector units work on the other: the second half's scores are formed
+      // while the first half is masked and reduced, and the first half's
+      // P V product runs while the second half's probabilities are formed.
+      // The arithmetic per query and its order are those of one 64-key pass.
+      auto tile_body = [&](auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        f32x4_t s[2][KB];
+        auto scores = [&](int kb) {
+          s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const int key = kb * 16 + q;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int key = kb * 16 + q;
+          for (int ks = 0; ks < HD / 32; ++ks) {
+            const int c = ks * 4 + gp;
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(sk + key * ROWB + ((c ^ fk(key)) << 4));
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
+          }
+        };
+        float mx[2] = {-INFINITY, -INFINITY};
+        auto mask_max = [&](int kb) {
 #pragma unroll
-        for (int ks = 0; ks < HD / 32; ++ks) {
-          const int c = ks * 4 + gp;
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(sk + key * ROWB + ((c ^ fk(key)) << 4));
-          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
-          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
-        }
-      }
-      // online softmax per query, in base-2 units (x = s * scale_log2, one
-      // fused multiply-add inside the exponent); the output accumulators are
-      // rescaled only when some query's running max grew -- otherwise alpha is
-      // exactly 1 for every lane and the multiply is skipped
-      bf16x8_t pb[2][KS];
-      bool grew = false;
-      float alpha[2];
-      // causal mask only on tiles that reach past some row's position
-      // (uniform: every wave of the workgroup has the same rows)
-      const bool masked = t0 + KT - 1 > pmin;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float mx = -INFINITY;
-        if (masked) {
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const int key = t0 + kb * 16 + 4 * gp + v;
-              const float x = key <= pos[b] ? s[b][kb][v] : -INFINITY;
-              s[b][kb][v] = x;
-              mx = fmaxf(mx, x);
+              if constexpr (MASKED) {
+                const int key = t0 + kb * 16 + 4 * gp + v;
+                s[b][kb][v] = key <= pos[b] ? s[b][kb][v] : -INFINITY;
+              }
+              mx[b] = fmaxf(mx[b], s[b][kb][v]);
             }
-        } else {
+        };
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB / 2; ++kb) scores(kb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[b][kb][v]);
+        for (int kb = KB / 2; kb < KB; ++kb) scores(kb);
+#pragma unroll
+        for (int kb = 0; kb < KB / 2; ++kb) mask_max(kb);
+        // second half's scores (K fragment reads + MFMAs) interleaved with the
+        // first half's mask and max
+#pragma unroll
+        for (int i = 0; i < (KB / 2) * (HD / 32); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, CB_ATTN_SG_B, 0);   // VALU
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[b], mx * scale_log2);
-        grew |= m_new > m_run[b];
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
-        alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use);
-        float sum = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = KB / 2; kb < KB; ++kb) mask_max(kb);
+        // online softmax per query, in base-2 units (x = s * scale_log2, one
+        // fused multiply-add inside the exponent)
+        bf16x8_t pb[2][KS];
+        float alpha[2], m_use[2], sum[2] = {0.f, 0.f};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][kb][v], scale_log2, -m_use));
-            s[b][kb][v] = e;
-            sum += e;
-          }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        l_run[b] = l_run[b] * alpha[b] + sum;
-        m_run[b] = m_new;
-        // P^T as the B operand: k slot j of lane group gp is key 32st+4gp+j
-        // (j<4) or 32st+16+4gp+(j-4), matching the V^T reads below
-#pragma unroll
-        for (int st = 0; st < KS; ++st)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            pb[b][st][v] = (__bf16)s[b][2 * st][v];
-            pb[b][st][4 + v] = (__bf16)s[b][2 * st + 1][v];
-          }
-      }
-      if (__any(grew)) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha[b];
-      }
-#pragma unroll
-      for (int mb = 0; mb < HD / 16; ++mb)
-#pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const int c = 2 * mb + (tc >> 1), h8 = (tc & 1) * 8;
-          const int k1 = 32 * st + tkey, k2 = k1 + 16;
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(sv + k1 * ROWB + ((c ^ fv(k1)) << 4) + h8));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(sv + k2 * ROWB + ((c ^ fv(k2)) << 4) + h8));
-          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
-          oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) {
+          float m = fmaxf(mx[b], __shfl_xor(mx[b], 16));
+          m = fmaxf(m, __shfl_xor(m, 32));
+          const float m_new = fmaxf(m_run[b], m * scale_log2);
+          m_use[b] = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
+          alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use[b]);
+          m_run[b] = m_new;
         }
+        // probabilities of the 32-key step st; P^T as the B operand: k slot j
+        // of lane group gp is key 32st+4gp+j (j<4) or 32st+16+4gp+(j-4),
+        // matching the V^T reads below
+        auto probs = [&](int st) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float e =
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][2 * st + h][v], scale_log2, -m_use[b]));
+                sum[b] += e;
+                pb[b][st][4 * h + v] = (__bf16)e;
+              }
+        };
+        // the output accumulators are rescaled by alpha (exactly 1 when the
+        // running max did not grow) right before the P V product adds to them
+        auto pv = [&](int st, bool rescale) {
+#pragma unroll
+          for (int mb = 0; mb < HD / 16; ++mb) {
+            const int c = 2 * mb + (tc >> 1), h8 = (tc & 1) * 8;
+            const int k1 = 32 * st + tkey, k2 = k1 + 16;
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s*)(sv + k1 * ROWB + ((c ^ fv(k1)) << 4) + h8));
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s*)(sv + k2 * ROWB + ((c ^ fv(k2)) << 4) + h8));
+            const bf16x8_t va =
+                __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            if (rescale) {
+              oacc[0][mb] *= alpha[0];
+              oacc[1][mb] *= alpha[1];
+            }
+            oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
+            oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
+          }
+        };
+        probs(0);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(0, true);
+        probs(1);
+        // first half's P V (transposing LDS reads + MFMAs, rescale) interleaved
+        // with the second half's probabilities
+#pragma unroll
+        for (int i = 0; i < HD / 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, CB_ATTN_SG_E, 0);   // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pv(1, false);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float t = sum[b];
+          t += __shfl_xor(t, 16);
+          t += __shfl_xor(t, 32);
+          l_run[b] = l_run[b] * alpha[b] + t;
+        }
+      };
+      // causal mask only on tiles that reach past some row's position
+      // (uniform: every wave of the workgroup has the same rows)
+      if (t0 + KT - 1 > pmin) tile_body(std::true_type{});
+      else tile_body(std::false_type{});
     }
   }
   CB_WAIT_VMCNT(0);
