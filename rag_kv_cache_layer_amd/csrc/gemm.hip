@@ -14,11 +14,11 @@
 // several K steps in flight; each wave waits only for its own loads of the
 // step it needs (vmcnt) and then meets the others at a plain barrier (a fenced
 // barrier would drain the ring).  Two tile shapes:
-//  * 128x128, K step 64, 3-stage ring, four waves of 64x64 (4x4 blocks of
+//  * 128x128, K step 64, 4-stage ring, four waves of 64x64 (4x4 blocks of
 //    v_mfma_f32_16x16x32_bf16): QKV, O and down projections;
-//  * 256x256, K step 32, 4-stage ring, four waves of 128x128 (accumulators
-//    in AGPRs): the gate/up projection, where N is large -- four times the
-//    matrix work per barrier.
+//  * 256x256, K step 32, 4-stage ring, eight waves of 128x64 (four waves of
+//    128x128 with the accumulators in AGPRs as a build option): the gate/up
+//    projection, where N is large -- four times the matrix work per barrier.
 // Tiles are numbered so that the M tiles sharing one weight tile run back to
 // back on the same XCD (workgroups are dealt round-robin to the 8 XCDs),
 // which keeps each weight tile in that XCD's L2 while it is reused.  Split-K
@@ -216,7 +216,7 @@ __device__ __forceinline__ int xcd_remap(int id, int nb) {
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
 #ifndef CB_GEMM_NSTAGE
-#define CB_GEMM_NSTAGE 3
+#define CB_GEMM_NSTAGE 4
 #endif
 #ifndef CB_GEMM_MINBLOCKS
 #define CB_GEMM_MINBLOCKS 1
@@ -343,7 +343,11 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
       if (it < nk) {
         // this wave's DMA for step `it` is done once at most the later
         // steps' 8 loads per step are outstanding
-        if (it + 1 < nk) CB_WAIT_VMCNT(8 * (NSTAGE - 2));
+        const int later = min(nk - 1 - it, NSTAGE - 2);
+        static_assert(NSTAGE <= 5, "wait counts below cover at most three later steps");
+        if (later >= 3) CB_WAIT_VMCNT(24);
+        else if (later == 2) CB_WAIT_VMCNT(16);
+        else if (later == 1) CB_WAIT_VMCNT(8);
         else CB_WAIT_VMCNT(0);
         CB_BARRIER();   // every wave's step `it` is in LDS; step it-1's buffer is free
         const bool more = it + NSTAGE - 1 < nk;
