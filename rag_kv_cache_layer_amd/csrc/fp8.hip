@@ -24,7 +24,10 @@ namespace cb {
 
 namespace {
 
-constexpr int QBM = 128, QBN = 128, QBK = 128, QNS = 3, QCLD = QBN + 4;
+#ifndef CB_FP8_NSTAGE
+#define CB_FP8_NSTAGE 3
+#endif
+constexpr int QBM = 128, QBN = 128, QBK = 128, QNS = CB_FP8_NSTAGE, QCLD = QBN + 4;
 constexpr int kQStage = (QBM + QBN) * QBK;                   // 32 KB
 constexpr int kQSmem = QNS * kQStage > QBM * QCLD * 4 ? QNS * kQStage : QBM * QCLD * 4;
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
@@ -168,7 +171,13 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt,
     for (int u = 0; u < QNS; ++u) {
       const int it = it0 + u;
       if (it < nk) {
-        if (it + 1 < nk) CB_WAIT_VMCNT(8 * (QNS - 2));
+        // this wave's loads of step it landed once at most the later steps'
+        // (8 loads each, only those actually issued) are outstanding
+        const int later = min(nk - 1 - it, QNS - 2);
+        static_assert(QNS >= 2 && QNS <= 5, "wait counts below cover at most three later steps");
+        if (later >= 3) CB_WAIT_VMCNT(24);
+        else if (later == 2) CB_WAIT_VMCNT(16);
+        else if (later == 1) CB_WAIT_VMCNT(8);
         else CB_WAIT_VMCNT(0);
         CB_BARRIER();
         if (it + QNS - 1 < nk) issue((u + QNS - 1) % QNS, kb + (it + QNS - 1) * QBK);
