@@ -71,6 +71,10 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 #ifndef CB_ATTN_SG_E
 #define CB_ATTN_SG_E 8
 #endif
+// workgroups the key split aims at when the (row tile, KV head) grid is small
+#ifndef CB_ATTN_WG_TARGET
+#define CB_ATTN_WG_TARGET 768
+#endif
 #ifndef CB_ATTN_SPLIT
 #define CB_ATTN_SPLIT 512
 #endif
@@ -610,7 +614,7 @@ int attn_key_split(int dtype, int m, int n_kv, int T) {
   // partial buffers hold T / kKeySplit splits).  At the 8B layer (128
   // groups, T = 3104) that is 6 parts of 576 keys: attention + merge 47 us,
   // against 55 us with 7 parts of 512 and 52 us with 4 of 832.
-  const int parts = std::max(1, (768 + groups / 2) / groups);
+  const int parts = std::max(1, (CB_ATTN_WG_TARGET + groups / 2) / groups);
   const int per = (T + parts - 1) / parts;
   return std::max(kKeySplit, (per + 63) / 64 * 64);
 }
