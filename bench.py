@@ -192,13 +192,20 @@ def main():
     # ---------------- timed region ----------------
     for _ in range(args.warmup):
         step()
+    # one hipEvent pair per step on the stream the library launches on (torch's
+    # current stream); the step time is the median of the per-step times
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         step()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    ms = float(np.median(step_ms))
+    ms_wall = (t1 - t0) * 1e3 / args.steps
 
     # per-kernel durations: the same steps again with hipEvents around every launch
     F.profile_begin()
@@ -347,6 +354,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_mean_wall": round(ms_wall, 5),
+        "ms_per_step_min_max": [round(float(step_ms.min()), 5), round(float(step_ms.max()), 5)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

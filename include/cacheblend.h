@@ -104,11 +104,18 @@ typedef struct {
 } cb_layer_weights;
 
 /* Device RoPE table: cos[p][hd/2], sin[p][hd/2] fp32 for p = 0 .. n_pos-1,
- * as written by cb_rope_table(cfg, 0, n_pos, ...) and copied to the device. */
+ * as written by cb_rope_table(cfg, 0, n_pos, ...) and copied to the device.
+ * head_dim and rope_theta name the configuration the table was built for;
+ * every call that takes a table returns CB_ERR_ARG unless both equal the
+ * call's cfg (a table of another base or head size would rotate by the
+ * wrong angles), and CB_ERR_SHAPE when n_pos is below the positions the
+ * call reads. */
 typedef struct {
   const float* cos;
   const float* sin;
   int32_t n_pos;
+  int32_t head_dim;
+  float rope_theta;
 } cb_rope_dev;
 
 /* ---------------------------------------------------------------------------

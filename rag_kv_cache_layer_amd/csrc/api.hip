@@ -181,8 +181,10 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
-cb_status check_rope(const cb_rope_dev* r, int need) {
+cb_status check_rope(const cb_layer_config* c, const cb_rope_dev* r, int need) {
   if (!r || !r->cos || !r->sin) return CB_ERR_ARG;
+  // a table is only valid for the base and head size it was built with
+  if (r->head_dim != c->head_dim || r->rope_theta != c->rope_theta) return CB_ERR_ARG;
   if (r->n_pos < need) return CB_ERR_SHAPE;
   return CB_OK;
 }
@@ -586,7 +588,7 @@ extern "C" cb_status cb_rope_shift(const cb_layer_config* cfg, const cb_rope_dev
   const Dims D(*cfg);
   if (n_layers > 1 && layer_stride_elems < (int64_t)T * D.kv_dim) return CB_ERR_SHAPE;
   if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
-  st = check_rope(rope, n_chunks > 1 ? chunk_offsets[n_chunks - 1] + 1 : 0);
+  st = check_rope(cfg, rope, n_chunks > 1 ? chunk_offsets[n_chunks - 1] + 1 : 0);
   if (st) return st;
   RopeShiftArgs a{};
   a.k_cache = k_cache;
@@ -760,7 +762,7 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
   const int n_cand = m_in - n_query;
   if (n_cand < 0 || n_cand > n_ctx - first_chunk_len) return CB_ERR_SHAPE;
   if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
-  st = check_rope(rope, T);
+  st = check_rope(cfg, rope, T);
   if (st) return st;
   if (ws_bytes < cb_workspace_size(cfg, T, m_in)) return CB_ERR_WORKSPACE;
   if (t_validate && m_in > 0) {
@@ -823,7 +825,7 @@ extern "C" cb_status cb_blend_layer_fp8(const cb_layer_config* cfg, const cb_lay
   const int n_query = T - n_ctx;
   const int n_cand = m_in - n_query;
   if (n_cand < 0 || n_cand > n_ctx - first_chunk_len) return CB_ERR_SHAPE;
-  st = check_rope(rope, T);
+  st = check_rope(cfg, rope, T);
   if (st) return st;
   if (ws_bytes < cb_workspace_size_fp8(cfg, T, m_in)) return CB_ERR_WORKSPACE;
   if (t_validate && m_in > 0) {
@@ -854,7 +856,7 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
     return CB_ERR_ARG;
   if (T < 0 || pos0 < 0) return CB_ERR_ARG;
   if (cfg->dtype == CB_F32 && T > kF32MaxT) return CB_ERR_UNSUPPORTED;
-  st = check_rope(rope, pos0 + T);
+  st = check_rope(cfg, rope, pos0 + T);
   if (st) return st;
   if (ws_bytes < cb_workspace_size(cfg, T, T)) return CB_ERR_WORKSPACE;
   if (T == 0) return CB_OK;
@@ -973,7 +975,7 @@ cb_status stack_run(const cb_layer_config* cfg, int32_t n_layers, const cb_layer
   if (n_layers > 1 && layer_stride_elems < layer_elems) return CB_ERR_SHAPE;
   if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
   if (src.fp8 && D.hd % 16) return CB_ERR_SHAPE;
-  st = check_rope(rope, T);
+  st = check_rope(cfg, rope, T);
   if (st) return st;
   if (ws_bytes < cb_stack_workspace_size(cfg, T)) return CB_ERR_WORKSPACE;
 
@@ -1204,7 +1206,7 @@ extern "C" cb_status cb_kv_from_fp8(const cb_layer_config* cfg, const cb_rope_de
   if (n_layers > 1 && layer_stride_elems < (int64_t)T * D.kv_dim) return CB_ERR_SHAPE;
   if ((layer_stride_elems * D.b) % 16) return CB_ERR_ARG;
   if (shift) {
-    st = check_rope(rope, n_chunks > 1 ? chunk_offsets[n_chunks - 1] + 1 : 0);
+    st = check_rope(cfg, rope, n_chunks > 1 ? chunk_offsets[n_chunks - 1] + 1 : 0);
     if (st) return st;
   }
   KvExpandArgs a{};
@@ -1259,7 +1261,7 @@ extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_w
     M_out += m_out[r];
     tiles += (m_out[r] + kAttnRowTile - 1) / kAttnRowTile;
   }
-  st = check_rope(rope, T_max);
+  st = check_rope(cfg, rope, T_max);
   if (st) return st;
   if (ws_bytes < cb_workspace_size(cfg, T_max, M_in)) return CB_ERR_WORKSPACE;
   if (t_validate && M_in > 0) {

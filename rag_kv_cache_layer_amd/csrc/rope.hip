@@ -24,12 +24,14 @@ struct ChunkOffsets {
 };
 
 // 8-element units per thread: two (32 B in flight per thread) measure ~20%
-// faster than one on a cold stack-wide launch and match a plain copy within 7%
+// faster than one on a cold stack-wide launch and match a plain copy within 7%.
+// A key row whose length is not a multiple of 8 * CB_ROPE_UPT elements (an
+// fp32 layout such as one KV head of 72) takes one unit per thread instead.
 #ifndef CB_ROPE_UPT
 #define CB_ROPE_UPT 2
 #endif
 
-template <typename T>
+template <typename T, int UPT>
 __global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int64_t lstride, int kv_dim,
                                                          int hd, int row0, int n_rows, int units_per_row,
                                                          int64_t total, const float* __restrict__ cosp,
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int6
   int64_t rr = u / units_per_row;
   int r = row0 + (int)(rr % n_rows);
   int l = (int)(rr / n_rows);
-  const int cu0 = cu * CB_ROPE_UPT;   // this thread's first 8-element unit of the row
+  const int cu0 = cu * UPT;   // this thread's first 8-element unit of the row
   // chunk of row r: the largest c in [1, n_chunks-1] with o[c] <= r
   int lo = 1, hi = n_chunks - 1;
   while (lo < hi) {
@@ -50,11 +52,11 @@ __global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int6
   }
   const int delta = offs.o[lo];
   T* p = k + (int64_t)l * lstride + (int64_t)r * kv_dim + cu0 * 8;
-  float v[CB_ROPE_UPT][8];
+  float v[UPT][8];
 #pragma unroll
-  for (int x = 0; x < CB_ROPE_UPT; ++x) load8(p + x * 8, v[x]);
+  for (int x = 0; x < UPT; ++x) load8(p + x * 8, v[x]);
 #pragma unroll
-  for (int x = 0; x < CB_ROPE_UPT; ++x) {
+  for (int x = 0; x < UPT; ++x) {
     const int e = ((cu0 + x) * 8) % hd;
     const float* cs = cosp + (int64_t)delta * (hd / 2) + e / 2;
     const float* sn = sinp + (int64_t)delta * (hd / 2) + e / 2;
@@ -83,18 +85,22 @@ hipError_t launch_rope_shift(int dtype, const RopeShiftArgs& a, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   ChunkOffsets offs;
   for (int c = 0; c <= a.n_chunks; ++c) offs.o[c] = a.offsets[c];
-  const int upr = a.kv_dim / 8 / CB_ROPE_UPT;   // threads per row (kv_dim is a multiple of 8 * CB_ROPE_UPT)
+  // kv_dim is a multiple of 8 (head_dim is); rows that do not split into
+  // whole CB_ROPE_UPT-unit groups use one unit per thread
+  const int upt = a.kv_dim % (8 * CB_ROPE_UPT) == 0 ? CB_ROPE_UPT : 1;
+  const int upr = a.kv_dim / 8 / upt;   // threads per row
   const int64_t total = (int64_t)a.n_layers * n_rows * upr;
   const int64_t blocks = (total + 255) / 256;
   LaunchScope ls("rope_shift", s);
-  if (dtype == CB_BF16)
-    rope_shift_kernel<bf16_t><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-        (bf16_t*)a.k_cache, a.layer_stride, a.kv_dim, a.hd, row0, n_rows, upr, total, a.cos, a.sin, offs,
-        a.n_chunks);
-  else
-    rope_shift_kernel<float><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-        (float*)a.k_cache, a.layer_stride, a.kv_dim, a.hd, row0, n_rows, upr, total, a.cos, a.sin, offs,
-        a.n_chunks);
+#define CB_ROPE_LAUNCH(T_, U_)                                                                                  \
+  rope_shift_kernel<T_, U_><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(                                        \
+      (T_*)a.k_cache, a.layer_stride, a.kv_dim, a.hd, row0, n_rows, upr, total, a.cos, a.sin, offs, a.n_chunks)
+  if (dtype == CB_BF16) {
+    if (upt == CB_ROPE_UPT) CB_ROPE_LAUNCH(bf16_t, CB_ROPE_UPT); else CB_ROPE_LAUNCH(bf16_t, 1);
+  } else {
+    if (upt == CB_ROPE_UPT) CB_ROPE_LAUNCH(float, CB_ROPE_UPT); else CB_ROPE_LAUNCH(float, 1);
+  }
+#undef CB_ROPE_LAUNCH
   return hipGetLastError();
 }
 

@@ -54,7 +54,13 @@ class LayerWeightsFp8(ctypes.Structure):
 
 
 class RopeDev(ctypes.Structure):
-    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32)]
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("n_pos", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_theta", ctypes.c_float)]
+
+
+def rope_dev(cfg: "LayerConfig", cos_ptr: int, sin_ptr: int, n_pos: int) -> RopeDev:
+    """cb_rope_dev for a table built for cfg (its head_dim and rope_theta)."""
+    return RopeDev(cos_ptr, sin_ptr, n_pos, cfg.head_dim, cfg.rope_theta)
 
 
 class BlendRequest(ctypes.Structure):
@@ -250,7 +256,7 @@ class DeviceRope:
         c, s = rope_table(cfg, 0, n_pos)
         self.cos = torch.from_numpy(c).to(device)
         self.sin = torch.from_numpy(s).to(device)
-        self.struct = RopeDev(self.cos.data_ptr(), self.sin.data_ptr(), n_pos)
+        self.struct = rope_dev(cfg, self.cos.data_ptr(), self.sin.data_ptr(), n_pos)
 
 
 class DeviceLayer:

@@ -81,7 +81,7 @@ FAKE = 1 << 20   # an aligned, never-dereferenced address: every case below fail
 
 
 def _blend(L, cfg, **over):
-    args = dict(w=F.LayerWeights(*([FAKE] * 9)), rope=F.RopeDev(FAKE, FAKE, 4096), k=FAKE, v=FAKE, T=100, n_ctx=90,
+    args = dict(w=F.LayerWeights(*([FAKE] * 9)), rope=F.rope_dev(cfg, FAKE, FAKE, 4096), k=FAKE, v=FAKE, T=100, n_ctx=90,
                 L0=30, s_in=FAKE, m_in=70, h_in=FAKE, in_rows=None, k_out=9, h_out=FAKE, dev=None, s_out=FAKE,
                 ws=FAKE, ws_bytes=1 << 40)
     args.update(over)
@@ -104,10 +104,10 @@ def test_blend_layer_argument_errors(cblib):
     assert _blend(L, cfg, L0=95)[0] == 2                                           # prefix past context
     assert _blend(L, cfg, m_in=5)[0] == 2                                          # misses query rows
     assert _blend(L, cfg, m_in=71)[0] == 2                                         # more rows than candidates
-    assert _blend(L, cfg, rope=F.RopeDev(FAKE, FAKE, 99))[0] == 2                  # table too short
+    assert _blend(L, cfg, rope=F.rope_dev(cfg, FAKE, FAKE, 99))[0] == 2                  # table too short
     assert _blend(L, cfg, ws_bytes=1000)[0] == 4
     assert _blend(L, _cfg(head_dim=96, n_q_heads=8, n_kv_heads=8))[0] == 5
-    assert _blend(L, _cfg(dtype="f32"), T=9000, n_ctx=8990, rope=F.RopeDev(FAKE, FAKE, 9000))[0] == 5
+    assert _blend(L, _cfg(dtype="f32"), T=9000, n_ctx=8990, rope=F.rope_dev(cfg, FAKE, FAKE, 9000))[0] == 5
     st, m = _blend(L, cfg, ws_bytes=1000)
     assert st == 4 and m == -7          # nothing written on failure before the size check
     st, m = _blend(L, cfg, m_in=10, k_out=3)   # all 10 rows are query rows: n_cand = 0 -> m_out = 10
@@ -117,13 +117,13 @@ def test_blend_layer_argument_errors(cblib):
 def test_other_calls_argument_errors(cblib):
     L, cfg = cblib, _cfg()
     offs = (ctypes.c_int32 * 3)(0, 40, 90)
-    rope_ok = F.RopeDev(FAKE, FAKE, 4096)
+    rope_ok = F.rope_dev(cfg, FAKE, FAKE, 4096)
     assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(rope_ok), None, 0, 1, 100, offs, 2, None) == 1
     bad = (ctypes.c_int32 * 3)(0, 50, 40)
     assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, 0, 1, 100, bad, 2, None) == 2
     over = (ctypes.c_int32 * 3)(0, 40, 101)
     assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, 0, 1, 100, over, 2, None) == 2
-    short = F.RopeDev(FAKE, FAKE, 40)
+    short = F.rope_dev(cfg, FAKE, FAKE, 40)
     assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(short), FAKE, 0, 1, 100, offs, 2, None) == 2
     assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, 10, 2, 100, offs, 2, None) == 2
     many = (ctypes.c_int32 * 258)(*range(258))
@@ -146,6 +146,27 @@ def test_other_calls_argument_errors(cblib):
     assert L.cb_filter_schedule(0, 1500, 0, 10, 5, None) == 1
 
 
+def test_rope_table_must_match_config(cblib):
+    """A device table built for another RoPE base or head size is refused by
+    every call that reads one (it would rotate by the wrong angles)."""
+    L, cfg = cblib, _cfg()
+    offs = (ctypes.c_int32 * 3)(0, 40, 90)
+    w = F.LayerWeights(*([FAKE] * 9))
+    good = F.rope_dev(cfg, FAKE, FAKE, 4096)
+    other_base = F.RopeDev(FAKE, FAKE, 4096, cfg.head_dim, 1e4)
+    other_hd = F.RopeDev(FAKE, FAKE, 4096, 128, cfg.rope_theta)
+    for bad in (other_base, other_hd):
+        assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(bad), FAKE, 0, 1, 100, offs, 2, None) == 1
+        assert _blend(L, cfg, rope=bad)[0] == 1
+        assert L.cb_full_prefill_layer(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(bad), FAKE, 100, 0, FAKE,
+                                       FAKE, FAKE, FAKE, 1 << 40, None) == 1
+        assert L.cb_kv_from_fp8(ctypes.byref(cfg), ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE,
+                                0, 100, offs, 2, 1, None) == 1
+    # the same table with matching fields passes the check (and fails later, on the workspace)
+    assert L.cb_full_prefill_layer(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(good), FAKE, 100, 0, FAKE,
+                                   FAKE, FAKE, FAKE, 16, None) == 4
+
+
 def test_profile_without_launches(cblib):
     F.profile_begin()
     assert F.profile_end() == {}
@@ -153,7 +174,7 @@ def test_profile_without_launches(cblib):
 
 def test_8bit_calls_argument_errors(cblib):
     L, cfg = cblib, _cfg()
-    rope_ok = F.RopeDev(FAKE, FAKE, 4096)
+    rope_ok = F.rope_dev(cfg, FAKE, FAKE, 4096)
     w8 = F.LayerWeightsFp8(*([FAKE] * 10))
     m = ctypes.c_int32(-7)
 
@@ -177,12 +198,12 @@ def test_8bit_calls_argument_errors(cblib):
               offs, 2, 1, None) == 1                                               # misaligned codes
     assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 50, 51, FAKE, FAKE, 0, 100, offs,
               2, 1, None) == 2                                                     # rows past T
-    short = F.RopeDev(FAKE, FAKE, 40)
+    short = F.rope_dev(cfg, FAKE, FAKE, 40)
     assert kv(ctypes.byref(cfg), ctypes.byref(short), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100, offs,
               2, 1, None) == 2                                                     # table too short for the shift
     cf72 = _cfg(dtype="f32", head_dim=72, n_q_heads=8, n_kv_heads=8, d_model=576)
     assert F.workspace_size(cf72, 10, 10) > 0
-    assert kv(ctypes.byref(cf72), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100,
+    assert kv(ctypes.byref(cf72), ctypes.byref(F.rope_dev(cf72, FAKE, FAKE, 4096)), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 100,
               offs, 2, 1, None) == 2                                               # head_dim not a multiple of 16
     many = (ctypes.c_int32 * 258)(*range(258))
     assert kv(ctypes.byref(cfg), ctypes.byref(rope_ok), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE, 0, 300, many,

@@ -85,7 +85,7 @@ def test_stack_rejects_bad_arguments_before_any_device_work(cblib):
     T = 144
     w = F.LayerWeights(*[0x20000 + 256 * i for i in range(9)])
     W = (F.LayerWeights * 2)(w, w)
-    rope = F.RopeDev(0x30000, 0x40000, T)
+    rope = F.rope_dev(cfg, 0x30000, 0x40000, T)
     offs = np.array([0, 64, 128], dtype=np.int32)
     ks = np.array([20, 20], dtype=np.int32)
     I32P = ctypes.POINTER(ctypes.c_int32)
@@ -102,13 +102,13 @@ def test_stack_rejects_bad_arguments_before_any_device_work(cblib):
     assert call(ks_=np.array([20, -1], dtype=np.int32)) == 1  # negative k_out
     assert call(n_layers=0) == 1
     assert call(stride=T * 256 - 8) == 2                      # layers overlap
-    assert call(rope_=F.RopeDev(0x30000, 0x40000, T - 1)) == 2
+    assert call(rope_=F.rope_dev(cfg, 0x30000, 0x40000, T - 1)) == 2
 
 
 def test_batch_rejects_bad_arguments_before_any_device_work(cblib):
     cfg = F.make_config(256, 4, 4, 64, 688, 1e4, 1e-5, "bf16")
     w = F.LayerWeights(*[0x20000 + 256 * i for i in range(9)])
-    rope = F.RopeDev(0x30000, 0x40000, 200)
+    rope = F.rope_dev(cfg, 0x30000, 0x40000, 200)
 
     def req(T=144, n_ctx=128, L0=64, m_in=36, k=20, kc=0x50000):
         return F.BlendRequest(kc, kc + 0x100000, T, n_ctx, L0, m_in, k)

@@ -17,6 +17,17 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("chunks,query,hd,nkv", [([37, 64, 0, 91], 5, 64, 2), ([512] * 6, 32, 128, 8),
                                                  ([1], 0, 64, 1), ([20], 3, 128, 2)])
 def test_shift_bit_exact(dtype, chunks, query, hd, nkv):
+    _shift_case(dtype, chunks, query, hd, nkv)
+
+
+@pytest.mark.parametrize("hd,nkv", [(72, 1), (8, 1), (24, 3), (40, 1)])
+def test_shift_rows_not_a_multiple_of_16(hd, nkv):
+    """fp32 key rows of 72, 8, 72 and 40 elements: every pair is rotated (the
+    kernel's unit per thread follows the row length)."""
+    _shift_case("f32", [37, 64, 21], 5, hd, nkv)
+
+
+def _shift_case(dtype, chunks, query, hd, nkv):
     need_gpu()
     p = synth.scaled(synth.PRESETS["llama8b_layer"], 256, nkv * 2, nkv, hd, 512, chunks, query).with_(dtype=dtype)
     cfg = F.config_of(p)

@@ -4,7 +4,11 @@
 * A reduced-width 4-layer stack against the oracle's stack: the first layer
   and the kept sets are compared exactly while both sides keep the same rows
   (the deviations of random weights are well separated at this size); the
-  driver must also equal calling the layers one by one.
+  driver must also equal calling the layers one by one.  The native stack
+  call (cb_blend_stack: caches resident, or loaded from pinned host memory
+  on a copy stream or the compute stream) and its 8-bit loader
+  (cb_blend_stack_kv8, codes from the oracle's quantizer) against the same
+  oracle stack.
 * The 32-layer 8B-shaped stack (8 x 512 + 64 tokens, r 0.30 -> 0.15) and the
   80-layer 70B-shaped stack (8 x 500 + 32, r = 0.15) at full size on seeded
   device-generated weights: properties that hold at any size -- nesting of the
@@ -72,6 +76,83 @@ def test_small_stack_matches_oracle_and_layer_calls():
         s, x = so, y
     torch.cuda.synchronize()
     assert torch.equal(K2, Kd) and torch.equal(V2, Vd) and torch.equal(x, out[-1]["y"])
+
+
+def _small_stack_oracle(seed, kv8=False):
+    """The reduced 4-layer stack's inputs and the oracle's stack on them.
+    With kv8 the chunk K/V are first stored as E4M3 codes by the oracle's
+    quantizer, and the oracle's stack runs on the values those codes expand
+    to (the caches an 8-bit loader delivers)."""
+    from oracle import fp8
+    p = synth.scaled(synth.PRESETS["llama8b_stack"], 512, 8, 2, 64, 1024, [60, 45, 70, 33], 7, n_layers=4)
+    st = "bf16"
+    L = p.n_layers
+    ws_ = [synth.layer_weights(p, seed, l) for l in range(L)]
+    order = synth.chunk_order(p, seed)
+    offs = synth.chunk_offsets(p, order)
+    kv = {c: blend.precompute_chunk(ws_, p, synth.chunk_embedding(p, seed, c), store=st) for c in order}
+    K, V = blend.assemble_caches(p, kv, order, p.T, L)
+    codes = None
+    if kv8:
+        codes = []
+        for X in (K, V):
+            q = [fp8.quantize_kv(x) for x in X]
+            codes.append((np.stack([c for c, _ in q]), np.stack([e for _, e in q])))
+        K = [fp8.expand_kv(c, e) for c, e in zip(*codes[0])]
+        V = [fp8.expand_kv(c, e) for c, e in zip(*codes[1])]
+    x_all = synth.context_embeddings(p, seed, order)
+    n_ctx, L0 = p.n_ctx, int(offs[1])
+    ks = blend.filter_schedule(L, 3000, 1500, n_ctx, n_ctx - L0)
+    want = blend.blend_stack(ws_, p, blend.shift_caches(p, K, offs, st), V, n_ctx, L0, x_all, ks, store=st)
+    return p, ws_, offs, K, V, codes, x_all, ks, want
+
+
+@pytest.mark.parametrize("mode", ["resident", "streamed", "streamed_same_stream", "kv8"])
+def test_native_stack_matches_oracle(mode):
+    """cb_blend_stack (caches resident, or each layer's chunk KV copied from
+    pinned host memory on a copy stream / on the compute stream) and
+    cb_blend_stack_kv8 (8-bit chunk KV expanded on the way in) against the
+    oracle's stack on the same inputs: the kept set of every layer exactly,
+    every layer's blended K/V and the last layer's output within the bf16
+    tolerance."""
+    need_gpu()
+    p, ws_, offs, K, V, codes, x_all, ks, want = _small_stack_oracle(23, kv8=(mode == "kv8"))
+    L, T, n_ctx, L0 = p.n_layers, p.T, p.n_ctx, int(offs[1])
+    cfg = F.config_of(p)
+    layers = [F.DeviceLayer(cfg, w) for w in ws_]
+    rope = F.DeviceRope(cfg, T)
+    wss = torch.empty(F.stack_workspace_size(cfg, T), dtype=torch.uint8, device="cuda")
+    x0 = dev(x_all[L0:], torch.bfloat16)
+    shape = (L, T, p.n_kv_heads, p.head_dim)
+    kw = {}
+    if mode == "resident":
+        Kd, Vd = dev(np.stack(K), torch.bfloat16), dev(np.stack(V), torch.bfloat16)
+    else:
+        Kd = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        Vd = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        if mode == "kv8":
+            (kc, ke), (vc, ve) = codes
+            pin = lambda a: torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+            kw = dict(k_src=pin(kc), v_src=pin(vc), k_src_exp=pin(ke), v_src_exp=pin(ve),
+                      copy_stream=torch.cuda.Stream())
+        else:
+            kw = dict(k_src=torch.from_numpy(np.stack(K)).to(torch.bfloat16).pin_memory(),
+                      v_src=torch.from_numpy(np.stack(V)).to(torch.bfloat16).pin_memory(),
+                      copy_stream=torch.cuda.Stream() if mode == "streamed" else None)
+    out = F.blend_stack_native(cfg, layers, rope, Kd, Vd, T, offs, x0, ks, wss, **kw)
+    torch.cuda.synchronize()
+    for l in range(L):
+        s_gpu = out[l]["s_out"].cpu().numpy()
+        assert np.array_equal(s_gpu, want["S"][l + 1] if l + 1 < L else want["s_last"]), (mode, l)
+        assert rel_err(host(Kd[l]), want["K"][l]) < 2e-2, (mode, l)
+        assert rel_err(host(Vd[l]), want["V"][l]) < 2e-2, (mode, l)
+        n_cand = int(np.sum(want["S"][l] < n_ctx))
+        d_gpu = host(out[l]["dev"])
+        assert rel_err(d_gpu[:n_cand], want["dev"][l][:n_cand]) < 2e-2, (mode, l)
+        # rows this layer did not recompute keep the shifted chunk cache bit for bit
+        untouched = np.setdiff1d(np.arange(T), want["S"][l])
+        assert np.array_equal(host(Vd[l])[untouched], np.stack(V)[l][untouched]), (mode, l)
+    assert rel_err(host(out[-1]["y"]), want["y"]) < 2e-2
 
 
 def _device_weights(cfg, p, n_layers, seed):
