@@ -46,6 +46,22 @@ def rel_err(x, y) -> float:
     return d / den if den > 0 else d
 
 
+def dev_consistent(dev_gpu, dev_ref, k_gpu_rows, k_ref_rows, slack=1e-4):
+    """Per-element pin of a deviation array: both sides compute dev_j =
+    ||K_new[j] - K_old[j]||^2 against the same K_old, so by the triangle
+    inequality |sqrt(dev_gpu_j) - sqrt(dev_ref_j)| <= ||K_gpu[j] - K_ref[j]||,
+    up to the fp32 rounding of the sums (slack, relative to sqrt(dev)).  This
+    holds for tiny deviations (rounding-level, as on a layer whose input is
+    context-free) as well as for large ones.  Returns the worst ratio of the
+    two sides (<= 1 when it holds)."""
+    a = np.sqrt(np.asarray(dev_gpu, np.float64))
+    b = np.sqrt(np.asarray(dev_ref, np.float64))
+    n = len(a)
+    dk = np.asarray(k_gpu_rows, np.float64).reshape(n, -1) - np.asarray(k_ref_rows, np.float64).reshape(n, -1)
+    bound = np.sqrt(np.sum(dk * dk, axis=1)) + slack * np.maximum(a, b) + 1e-30
+    return float(np.max(np.abs(a - b) / bound)) if n else 0.0
+
+
 def single_layer_case(p, seed: int, prepass_inputs: bool = True):
     """Weights, the shifted cache, hidden inputs and geometry of one layer.
 
