@@ -350,6 +350,27 @@ cb_status cb_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t* a, const i
                       const uint8_t* b, const int32_t* b_exp, void* c, int32_t ldc, int32_t out_dtype,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* cb_gemm_fp8 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same product, the same kernels and the same bits as cb_gemm_fp8; the
+ * split-K partials that cb_gemm_fp8 keeps in the caller's workspace live
+ * instead in a static device array of CB_GEMM_FP8_SCRATCH_BYTES inside the
+ * library, one copy per GPU, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine); the
+ * device address of the current device's copy is looked up once per device,
+ * on the first call made with that device current.
+ *  Arguments, layouts and results as cb_gemm_fp8; `stream` must belong to
+ *  the current device.  CB_ERR_WORKSPACE when the partials
+ *  (cb_gemm_fp8_workspace_size(M, N, K) bytes) exceed the static array;
+ *  other errors as cb_gemm_fp8.  Every call on one GPU shares that GPU's
+ *  array: calls whose work overlaps in time on one GPU (different streams,
+ *  or different host threads, without ordering between them) race on it and
+ *  give unspecified results.  Calls ordered on one stream are safe. */
+#define CB_GEMM_FP8_SCRATCH_BYTES (32u << 20)
+cb_status cb_gemm_fp8_noalloc(int32_t M, int32_t N, int32_t K, const uint8_t* a, const int32_t* a_exp,
+                              const uint8_t* b, const int32_t* b_exp, void* c, int32_t ldc,
+                              int32_t out_dtype, void* stream);
+
 /* The fusor over a stack of n_layers layers (section 4.3, Figure 9), with
  * each layer's KV loaded while the previous layer is recomputed (section 5,
  * Figure 11: the fusor waits for the previous layer's recompute and for the

@@ -1413,3 +1413,75 @@ extern "C" cb_status cb_gemm_fp8(int32_t M, int32_t N, int32_t K, const uint8_t*
   }
   return hip_status(launch_gemm_fp8(g, out_dtype, (hipStream_t)stream));
 }
+
+// ---------------------------------------------------------------------------
+// cb_gemm_fp8_noalloc: the split-K partials in a static device array
+// ---------------------------------------------------------------------------
+namespace cb {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+
+// One copy per GPU, alive until the process ends.  Host code never uses this
+// name as an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[CB_GEMM_FP8_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+cb_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return CB_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return CB_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CB_OK;
+}
+
+}  // namespace
+}  // namespace cb
+
+extern "C" cb_status cb_gemm_fp8_noalloc(int32_t M, int32_t N, int32_t K, const uint8_t* a, const int32_t* a_exp,
+                                         const uint8_t* b, const int32_t* b_exp, void* c, int32_t ldc,
+                                         int32_t out_dtype, void* stream) {
+  using namespace cb;
+  // the same checks as cb_gemm_fp8, then the scratch limit, all before any HIP call
+  if (M < 0 || N < 0 || K < 0 || ldc < N) return CB_ERR_ARG;
+  if (out_dtype != CB_F32 && out_dtype != CB_BF16) return CB_ERR_ARG;
+  if (M == 0 || N == 0) return CB_OK;
+  if (!a || !a_exp || !b || !b_exp || !c) return CB_ERR_ARG;
+  if (K % 16 || !aligned16(a) || !aligned16(b)) return CB_ERR_SHAPE;
+  if ((int64_t)M * K >= (int64_t)1 << 31 || (int64_t)N * K >= (int64_t)1 << 31) return CB_ERR_UNSUPPORTED;
+  const size_t need = cb_gemm_fp8_workspace_size(M, N, K);
+  if (need > (size_t)CB_GEMM_FP8_SCRATCH_BYTES) return CB_ERR_WORKSPACE;
+  Fp8GemmArgs g{};
+  g.A = a;
+  g.a_exp = a_exp;
+  g.B = b;
+  g.b_exp = b_exp;
+  g.C = c;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ldc = ldc;
+  g.splits = fp8_splits(N, K);
+  if (g.splits > 1) {
+    // every partial the finishing pass reads is written first by the same
+    // launch sequence, so nothing has to start at zero
+    void* p = nullptr;
+    const cb_status st = static_scratch(&p);
+    if (st) return st;
+    g.part = (float*)p;
+  }
+  return hip_status(launch_gemm_fp8(g, out_dtype, (hipStream_t)stream));
+}

@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
         "cb_quantize_fp8": (I32, [I32, P, I32, I32, P, P, P]),
         "cb_gemm_fp8_workspace_size": (SZ, [I32, I32, I32]),
         "cb_gemm_fp8": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P, SZ, P]),
+        "cb_gemm_fp8_noalloc": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P]),
         "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
         "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
                                  P, P]),
@@ -638,4 +639,22 @@ def gemm_fp8(a, a_exp, b, b_exp, out, ws=None, stream=None):
                              _dptr(out, "out", None, M * out.stride(0)), out.stride(0), od,
                              _dptr(ws, "ws") if need else None, ws.numel() if need else 0, _stream(stream)),
            "cb_gemm_fp8")
+    return out
+
+
+GEMM_FP8_SCRATCH_BYTES = 32 << 20   # CB_GEMM_FP8_SCRATCH_BYTES
+
+
+def gemm_fp8_noalloc(a, a_exp, b, b_exp, out, stream=None):
+    """cb_gemm_fp8_noalloc: gemm_fp8 with the split-K partials in the
+    library's static per-GPU array (no workspace argument, no allocation)."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    od = CB_BF16 if out.dtype == torch.bfloat16 else CB_F32
+    _check(lib().cb_gemm_fp8_noalloc(M, N, K, _dptr(a, "a", torch.uint8, M * K),
+                                     _dptr(a_exp, "a_exp", torch.int32, M), _dptr(b, "b", torch.uint8, N * K),
+                                     _dptr(b_exp, "b_exp", torch.int32, N),
+                                     _dptr(out, "out", None, M * out.stride(0)), out.stride(0), od,
+                                     _stream(stream)), "cb_gemm_fp8_noalloc")
     return out

@@ -219,6 +219,22 @@ def test_8bit_calls_argument_errors(cblib):
                                 None) == 1
 
 
+def test_gemm_fp8_noalloc_argument_errors(cblib):
+    L = cblib
+    g = lambda M, N, K, a=FAKE, ldc=None, od=0: L.cb_gemm_fp8_noalloc(M, N, K, a, FAKE, FAKE, FAKE, FAKE,
+                                                                        N if ldc is None else ldc, od, None)
+    assert g(-1, 16, 16) == 1
+    assert g(4, 16, 16, ldc=8) == 1
+    assert g(4, 16, 16, od=7) == 1
+    assert g(4, 16, 16, a=None) == 1
+    assert g(4, 16, 24) == 2                                   # K not a multiple of 16
+    assert g(4, 16, 16, a=FAKE + 4) == 2                       # misaligned codes
+    assert g(0, 16, 16) == 0                                   # nothing to do
+    # split-K partials beyond the static array: 2 x 1100 x 4096 x 4 B > 32 MiB
+    assert int(L.cb_gemm_fp8_workspace_size(1100, 4096, 4096)) > F.GEMM_FP8_SCRATCH_BYTES
+    assert g(1100, 4096, 4096) == 4
+
+
 def test_validate_switch(cblib):
     assert F.set_validate(True) is False
     assert F.set_validate(False) is True
