@@ -63,6 +63,10 @@ def parse():
                     help="also time the CPU oracle on the other workloads: the tiny fp32 layer (1 thread and all), "
                          "full prefill of the 8B layer, the 4-chunk sweep layer at r = 0.15 and 1, and spot layers "
                          "of the 32-layer 8B and 80-layer 70B stacks (scaled by the layer count, an estimate)")
+    ap.add_argument("--hbm-only", action="store_true",
+                    help="only the cold, large launches of the bandwidth-bound kernels (stack-wide RoPE shift, "
+                         "deviation over 15872 candidates, 8-bit KV expansion of the stack) and the streaming "
+                         "copy they are compared with; one JSON line")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one untimed 512 MiB device-to-device copy first (a known-size reference "
                          "for the HBM byte counters)")
@@ -117,6 +121,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     F.lib()   # fails loudly when the library is missing
+    if args.hbm_only:
+        out = hbm_kernels_measure()
+        print(json.dumps(out))
+        return
     log("library loaded; generating inputs")
     p = synth.PRESETS["llama8b_layer"]
     seed = args.seed
@@ -250,9 +258,7 @@ def main():
             F.full_prefill_layer(cfg, layer, rope, h_full, T, 0, kf, vf, h2, ws)
         torch.cuda.synchronize()
         extra["full_prefill_ms"] = round((time.perf_counter() - t0) * 100, 4)
-        extra["shift_stack"] = shift_stack_measure()
-        extra["kdev_cold"] = kdev_cold_measure()
-        extra["kv_expand_stack"] = kv_expand_measure()
+        extra.update(hbm_kernels_measure())
 
     if args.batch > 1:
         # n_req requests of the same shape (own caches, same rows): one shift
@@ -376,6 +382,52 @@ def main():
     }
     out.update(extra)
     print(json.dumps(out))
+
+
+def copy_cold_measure(reps=6, nbytes=1 << 30):
+    """cb_stream_copy (the library's streaming copy: 16-byte accesses, 1 KB
+    of contiguous memory per wave instruction, non-temporal stores) of 1 GiB,
+    rotating over four 1 GiB buffers so that no call finds its data in the
+    256 MB Infinity Cache; hipMemcpy's device-to-device copy beside it.
+    Bytes moved = read + write = 2 GiB per call."""
+    import torch
+    from rag_kv_cache_layer_amd import fusor as F
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    F.stream_copy(bufs[0], bufs[1])
+    torch.cuda.synchronize()
+
+    def med(fn):
+        times = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+    ms = med(lambda i: F.stream_copy(bufs[(2 * i) % 4], bufs[(2 * i + 1) % 4]))
+    ms_d2d = med(lambda i: bufs[(2 * i + 1) % 4].copy_(bufs[(2 * i) % 4]))
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": 2 * nbytes, "ms": round(ms, 4), "gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "hipmemcpy_d2d_gbs": round(2 * nbytes / (ms_d2d * 1e-3) / 1e9, 1)}
+
+
+def hbm_kernels_measure():
+    """Cold, large launches of the bandwidth-bound kernels, each with its rate
+    as a fraction of the 8 TB/s peak and of the streaming copy's rate."""
+    out = {"copy_cold": copy_cold_measure()}
+    ceiling = out["copy_cold"]["gbs"]
+    out["shift_stack"] = shift_stack_measure()
+    out["kdev_cold"] = kdev_cold_measure()
+    out["kv_expand_stack"] = kv_expand_measure()
+    for k in ("shift_stack", "kdev_cold", "kv_expand_stack"):
+        out[k]["frac_of_copy"] = round(out[k]["gbs"] / ceiling, 4)
+    return out
 
 
 def shift_stack_measure(reps=6):

@@ -214,6 +214,15 @@ typedef struct {
 cb_status cb_profile_begin(void);
 int32_t cb_profile_end(cb_kernel_stat* out, int32_t max_out);
 
+/* Measurement reference (not a step of the fusor): copies `bytes` bytes from
+ * src to dst (device, 16-byte aligned, bytes a multiple of 16; CB_ERR_ARG
+ * otherwise; the ranges must not overlap) with a plain streaming kernel:
+ * 16-byte accesses, each wave instruction over 1 KB of contiguous memory,
+ * non-temporal stores.  Its rate on large, cold buffers is the HBM ceiling
+ * the bandwidth-bound calls (cb_rope_shift, the deviation of cb_select_hkvd,
+ * cb_kv_from_fp8) are compared with.  Asynchronous on `stream`. */
+cb_status cb_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Device calls
  * ------------------------------------------------------------------------- */

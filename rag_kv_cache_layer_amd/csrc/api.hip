@@ -1485,3 +1485,10 @@ extern "C" cb_status cb_gemm_fp8_noalloc(int32_t M, int32_t N, int32_t K, const 
   }
   return hip_status(launch_gemm_fp8(g, out_dtype, (hipStream_t)stream));
 }
+
+extern "C" cb_status cb_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  using namespace cb;
+  if (bytes == 0) return CB_OK;
+  if (!src || !dst || bytes % 16 || !aligned16(src) || !aligned16(dst)) return CB_ERR_ARG;
+  return hip_status(launch_stream_copy(src, dst, bytes, (hipStream_t)stream));
+}

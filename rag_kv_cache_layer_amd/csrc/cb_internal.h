@@ -341,4 +341,7 @@ int attn_key_split(int dtype, int m, int n_kv, int T);
 size_t attn_part_rows(int n_q, int n_kv);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
+// Streaming copy of bytes / 16 16-byte units (bytes % 16 == 0, both 16-byte aligned).
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
 }  // namespace cb

@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
         "cb_gemm_fp8_workspace_size": (SZ, [I32, I32, I32]),
         "cb_gemm_fp8": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P, SZ, P]),
         "cb_gemm_fp8_noalloc": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P]),
+        "cb_stream_copy": (I32, [P, P, SZ, P]),
         "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
         "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
                                  P, P]),
@@ -361,6 +362,14 @@ def rope_shift(cfg: LayerConfig, rope: DeviceRope, k_cache, layer_stride: int, n
                                _dptr(k_cache, "k_cache", torch_dtype(cfg), need), layer_stride, n_layers, T,
                                offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(offs) - 1,
                                _stream(stream)), "cb_rope_shift")
+
+
+def stream_copy(src, dst, stream=None):
+    """cb_stream_copy: dst <- src (same byte size), the HBM reference copy."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("stream_copy: sizes differ")
+    _check(lib().cb_stream_copy(_dptr(src, "src"), _dptr(dst, "dst"), n, _stream(stream)), "cb_stream_copy")
 
 
 def select_hkvd(cfg: LayerConfig, k_new, k_ref, T: int, cand_rows, n: int, k: int, dev, sel_out, ws, stream=None):
