@@ -214,6 +214,50 @@ typedef struct {
 cb_status cb_profile_begin(void);
 int32_t cb_profile_end(cb_kernel_stat* out, int32_t max_out);
 
+/* ---------------------------------------------------------------------------
+ * Deviation analytics (diagnostics around the fusor, not steps of it;
+ * section 4.1 attention deviation, Figure 7 deviation concentration,
+ * section 4.3 / Figure 8 rank correlation across layers)
+ * ------------------------------------------------------------------------- */
+
+/* Byte offset in a workspace where cb_blend_layer (called with this T) and
+ * cb_full_prefill_layer (over T rows) leave the Q of the rows they
+ * recomputed: [rows][n_q_heads * head_dim] in cfg->dtype, RoPE applied at
+ * each row's position, rows in the order of s_in (blend; the query rows are
+ * the last T - n_ctx) or 0 .. T-1 (full prefill).  Valid until the next call
+ * that uses the workspace.  0 on invalid cfg or T <= 0. */
+size_t cb_workspace_q_offset(const cb_layer_config* cfg, int32_t T);
+
+/* Workspace bytes for cb_attention_deviation over m rows of n_q heads and for
+ * cb_spearman / cb_top_share over n values (the larger of the two). */
+size_t cb_analytics_workspace_size(int32_t m, int32_t n_q, int32_t n);
+
+/* Attention deviation (section 4.1): with A_x[i][h][t] = softmax over
+ * t <= last_key[i] of q_x[i,h] . k_x[t, h / (n_q/n_kv)] / sqrt(head_dim) and
+ * 0 for t > last_key[i], writes out[0] = ||A_a - A_b||_F^2 and out[1] =
+ * ||A_b||_F^2 (device double [2]; the relative deviation is
+ * sqrt(out[0] / out[1])).  q_a, q_b: device [m][n_q][hd]; k_a, k_b: device
+ * [T][n_kv][hd] (cfg dtype); last_key: device int32 [m], clamped to
+ * [0, T-1].  Scores and probabilities in fp32, sums in fp64 in a fixed
+ * order.  ws: device, >= cb_analytics_workspace_size(m, n_q, 0) bytes. */
+cb_status cb_attention_deviation(const cb_layer_config* cfg, int32_t m, const void* q_a, const void* k_a,
+                                 const void* q_b, const void* k_b, int32_t T, const int32_t* last_key,
+                                 double* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Spearman's rank correlation of x and y (device fp32 [n], finite values):
+ * Pearson's correlation of their average ranks (tied values share the mean
+ * of the ranks they span), fp64, written to out (device double [1]; NaN
+ * when a rank vector is constant).  ws >= cb_analytics_workspace_size(0, 0,
+ * n) bytes. */
+cb_status cb_spearman(const float* x, const float* y, int32_t n, double* out, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Share of sum(x) held by the k largest values of x (device fp32 [n],
+ * finite; 0 <= k <= n): out[0] (device double) = that sum / sum(x), NaN when
+ * sum(x) <= 0.  ws >= cb_analytics_workspace_size(0, 0, n) bytes. */
+cb_status cb_top_share(const float* x, int32_t n, int32_t k, double* out, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* Measurement reference (not a step of the fusor): copies `bytes` bytes from
  * src to dst (device, 16-byte aligned, bytes a multiple of 16; CB_ERR_ARG
  * otherwise; the ranges must not overlap) with a plain streaming kernel:

@@ -9,17 +9,17 @@ Diagnostics around the fusor, run on the device with random weights:
 * Spearman's rank correlation of the KV deviation between neighbouring
   layers (section 4.3, Figure 8).
 
-The stacks run through the library (cb_full_prefill_layer, cb_blend_layer);
-the statistics are small torch reductions on the results (fp32 attention
-probabilities, fp64 sums).  The query rows' Q for the attention matrices is
-projected here from each layer's stored input rows (RMSNorm, W_q, RoPE from
-the library's own cos/sin tables), the same way for the blended and the
-full-prefill run.
+Every step runs in the library: the layers (cb_full_prefill_layer,
+cb_blend_layer), the query rows' Q (the Q those calls computed, read from
+their workspace: cb_workspace_q_offset), the attention deviation
+(cb_attention_deviation), ranks and correlation (cb_spearman) and the top
+shares (cb_top_share).  torch holds the buffers; this module only sequences
+the calls and copies results.
 """
 from __future__ import annotations
 
 import math
-from typing import Dict, List, Sequence
+from typing import Dict, Sequence
 
 from . import fusor as F
 
@@ -27,70 +27,6 @@ from . import fusor as F
 def _torch():
     import torch
     return torch
-
-
-def attention_matrix(q, k, last_key):
-    """P [m][n_q][T] = softmax over t <= last_key[i] of q[i,h] . k[t, h // g] /
-    sqrt(hd) (0 past last_key[i]); q [m][n_q][hd], k [T][n_kv][hd], fp32."""
-    torch = _torch()
-    m, n_q, hd = q.shape
-    T, n_kv, _ = k.shape
-    g = n_q // n_kv
-    kt = k.float().permute(1, 2, 0).contiguous()                       # [n_kv][hd][T]
-    s = torch.matmul(q.float().reshape(m, n_kv, g, hd), kt) / math.sqrt(hd)   # [m][n_kv][g][T]
-    t = torch.arange(T, device=q.device)
-    last = torch.as_tensor(last_key, device=q.device).reshape(m, 1, 1, 1)
-    s = s.masked_fill(t.reshape(1, 1, 1, T) > last, float("-inf"))
-    return torch.softmax(s, dim=-1).reshape(m, n_q, T)
-
-
-def attention_deviation(a, b) -> float:
-    """L-2 (Frobenius) norm of a - b."""
-    d = (a.double() - b.double())
-    return float(d.pow(2).sum().sqrt())
-
-
-def ranks(x):
-    """1-based ascending ranks; ties share the mean of the ranks they span."""
-    torch = _torch()
-    vals, inv, counts = torch.unique(x.double(), sorted=True, return_inverse=True, return_counts=True)
-    ends = torch.cumsum(counts, 0).double()
-    starts = ends - counts.double()
-    return ((starts + 1.0 + ends) / 2.0)[inv]
-
-
-def spearman(x, y) -> float:
-    rx, ry = ranks(x), ranks(y)
-    rx = rx - rx.mean()
-    ry = ry - ry.mean()
-    den = math.sqrt(float((rx * rx).sum()) * float((ry * ry).sum()))
-    return float((rx * ry).sum()) / den if den > 0 else float("nan")
-
-
-def top_share(dev, frac: float) -> float:
-    """Share of the summed deviation held by the ceil(frac * n) largest."""
-    torch = _torch()
-    d = torch.sort(dev.double(), descending=True).values
-    n = int(math.ceil(frac * d.numel() - 1e-9))
-    tot = float(d.sum())
-    return float(d[:n].sum()) / tot if tot > 0 else float("nan")
-
-
-def query_q(cfg, layer: F.DeviceLayer, rope: F.DeviceRope, x, positions):
-    """Q [m][n_q][hd] (fp32) of rows x [m][d] at the given positions:
-    RMSNorm with the layer's gain, W_q, RoPE on interleaved pairs."""
-    torch = _torch()
-    xf = x.float()
-    xn = xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + cfg.rms_eps) * layer.t["attn_norm"]
-    q = torch.matmul(xn, layer.t["w_q"].float().t().contiguous()).reshape(x.shape[0], cfg.n_q_heads, cfg.head_dim)
-    pos = torch.as_tensor(positions, device=x.device).long()
-    c = rope.cos[pos].unsqueeze(1)   # [m][1][hd/2]
-    s = rope.sin[pos].unsqueeze(1)
-    a, b = q[..., 0::2], q[..., 1::2]
-    out = torch.empty_like(q)
-    out[..., 0::2] = a * c - b * s
-    out[..., 1::2] = a * s + b * c
-    return out
 
 
 def precompute_chunks(cfg, layers, rope, x_all, offs, ws):
@@ -114,23 +50,51 @@ def precompute_chunks(cfg, layers, rope, x_all, offs, ws):
     return K, V
 
 
-def full_stack(cfg, layers, rope, x_all, ws):
-    """Full prefill through the stack: per-layer K, V and each layer's input."""
+def full_stack(cfg, layers, rope, x_all, n_ctx, ws):
+    """Full prefill through the stack: per-layer K, V and the Q of the query
+    rows n_ctx .. T-1 as the library computed them."""
     torch = _torch()
     T = x_all.shape[0]
     kv = (T, cfg.n_kv_heads, cfg.head_dim)
-    Ks, Vs, xs = [], [], []
+    Ks, Vs, Qs = [], [], []
     x = x_all
     for layer in layers:
         k = torch.empty(kv, dtype=x.dtype, device=x.device)
         v = torch.empty_like(k)
         y = torch.empty_like(x)
         F.full_prefill_layer(cfg, layer, rope, x, T, 0, k, v, y, ws)
+        Qs.append(F.workspace_q(cfg, ws, T, T)[n_ctx:].clone())
         Ks.append(k)
         Vs.append(v)
-        xs.append(x)
         x = y
-    return Ks, Vs, xs
+    return Ks, Vs, Qs
+
+
+def blend_stack(cfg, layers, rope, K, V, T, offs, x_first, ks, ws):
+    """The fusor through the stack (re-alignment of every layer's keys, then
+    gradual filtering, as fusor.blend_stack), keeping per layer the Q of the
+    query rows and the deviations of the recomputed candidates."""
+    torch = _torch()
+    offs = [int(o) for o in offs]
+    n_ctx, L0 = offs[-1], offs[1]
+    q = T - n_ctx
+    kv = cfg.n_kv_heads * cfg.head_dim
+    F.rope_shift(cfg, rope, K, T * kv, len(layers), T, offs)
+    dev_ = x_first.device
+    s = torch.arange(L0, T, dtype=torch.int32, device=dev_)
+    x = x_first
+    Qs, devs = [], []
+    for l, layer in enumerate(layers):
+        m_in = s.numel()
+        m_out = F.expected_m_out(T, n_ctx, m_in, ks[l])
+        y = torch.empty((m_out, cfg.d_model), dtype=F.torch_dtype(cfg), device=dev_)
+        so = torch.empty(m_out, dtype=torch.int32, device=dev_)
+        dv = torch.empty(m_in, dtype=torch.float32, device=dev_)
+        F.blend_layer(cfg, layer, rope, K[l], V[l], T, n_ctx, L0, s, m_in, x, None, ks[l], y, dv, so, ws)
+        Qs.append(F.workspace_q(cfg, ws, T, m_in)[m_in - q:].clone())
+        devs.append(dv[:m_in - q])
+        s, x = so, y
+    return Qs, devs
 
 
 def stack_study(cfg, layers: Sequence[F.DeviceLayer], rope: F.DeviceRope, x_all, offs: Sequence[int],
@@ -150,33 +114,28 @@ def stack_study(cfg, layers: Sequence[F.DeviceLayer], rope: F.DeviceRope, x_all,
     T = x_all.shape[0]
     offs = [int(o) for o in offs]
     n_ctx, L0 = offs[-1], offs[1]
-    n_cand, q = n_ctx - L0, T - n_ctx
+    n_cand = n_ctx - L0
     L = len(layers)
     ws = F.workspace(cfg, T, T, x_all.device)
     K0, V0 = precompute_chunks(cfg, layers, rope, x_all, offs, ws)
-    Kf, Vf, xf = full_stack(cfg, layers, rope, x_all, ws)
-    qpos = list(range(n_ctx, T))
-    A_full, A_norm = [], []
-    for l in range(L):
-        a = attention_matrix(query_q(cfg, layers[l], rope, xf[l][n_ctx:], qpos), Kf[l], qpos)
-        A_full.append(a)
-        A_norm.append(float(a.double().pow(2).sum().sqrt()))
+    Kf, Vf, Qf = full_stack(cfg, layers, rope, x_all, n_ctx, ws)
+    last = torch.arange(n_ctx, T, dtype=torch.int32, device=x_all.device)
     out = {"ratios_e4": list(ratios_e4), "attn_dev": [], "attn_dev_mean": []}
     dev_r1 = None
     for r in ratios_e4:
         ks = F.filter_schedule(L, r, r, n_ctx, n_cand)
         K, V = K0.clone(), V0.clone()
-        res = F.blend_stack(cfg, layers, rope, K, V, T, offs, x_all[L0:].contiguous(), ks, ws)
+        Qb, devs = blend_stack(cfg, layers, rope, K, V, T, offs, x_all[L0:].contiguous(), ks, ws)
         per = []
         for l in range(L):
-            x_in = x_all[n_ctx:] if l == 0 else res[l - 1]["y"][-q:]
-            a = attention_matrix(query_q(cfg, layers[l], rope, x_in, qpos), K[l], qpos)
-            per.append(attention_deviation(a, A_full[l]) / A_norm[l])
+            d2, n2 = F.attention_deviation(cfg, Qb[l], K[l], Qf[l], Kf[l], last)
+            per.append(math.sqrt(d2 / n2))
         out["attn_dev"].append(per)
         out["attn_dev_mean"].append(sum(per) / L)
         if r >= 10000:
-            dev_r1 = [res[l]["dev"][:n_cand].clone() for l in range(L)]
+            dev_r1 = devs
     if dev_r1 is not None:
-        out["top_share"] = {str(f): [top_share(d, f) for d in dev_r1] for f in top_fracs}
-        out["spearman_neighbours"] = [spearman(dev_r1[l], dev_r1[l + 1]) for l in range(1, L - 1)]
+        out["top_share"] = {str(f): [F.top_share(d, int(math.ceil(f * d.numel() - 1e-9))) for d in dev_r1]
+                            for f in top_fracs}
+        out["spearman_neighbours"] = [F.spearman(dev_r1[l], dev_r1[l + 1]) for l in range(1, L - 1)]
     return out

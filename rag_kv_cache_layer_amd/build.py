@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcacheblend.so")
-SOURCES = ("rope.hip", "norm.hip", "select.hip", "gemm.hip", "attn.hip", "fp8.hip", "kv8.hip", "copy.hip", "api.hip")
+SOURCES = ("rope.hip", "norm.hip", "select.hip", "gemm.hip", "attn.hip", "fp8.hip", "kv8.hip", "copy.hip", "analytics.hip", "api.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE,

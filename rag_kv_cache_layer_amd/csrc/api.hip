@@ -1492,3 +1492,49 @@ extern "C" cb_status cb_stream_copy(const void* src, void* dst, size_t bytes, vo
   if (!src || !dst || bytes % 16 || !aligned16(src) || !aligned16(dst)) return CB_ERR_ARG;
   return hip_status(launch_stream_copy(src, dst, bytes, (hipStream_t)stream));
 }
+
+// ---------------------------------------------------------------------------
+// deviation analytics
+// ---------------------------------------------------------------------------
+
+extern "C" size_t cb_workspace_q_offset(const cb_layer_config* cfg, int32_t T) {
+  using namespace cb;
+  if (check_cfg(cfg) != CB_OK || T <= 0) return 0;
+  return layout(*cfg, T, T).q;
+}
+
+extern "C" size_t cb_analytics_workspace_size(int32_t m, int32_t n_q, int32_t n) {
+  if (m < 0 || n_q < 0 || n < 0) return 0;
+  const size_t a = (size_t)m * n_q * 2, b = (size_t)n * 2;
+  return (a > b ? a : b) * sizeof(double) + 256;
+}
+
+extern "C" cb_status cb_attention_deviation(const cb_layer_config* cfg, int32_t m, const void* q_a, const void* k_a,
+                                            const void* q_b, const void* k_b, int32_t T, const int32_t* last_key,
+                                            double* out, void* ws, size_t ws_bytes, void* stream) {
+  using namespace cb;
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (m < 0 || T <= 0 || !out) return CB_ERR_ARG;
+  if (m == 0) return CB_OK;
+  if (!q_a || !k_a || !q_b || !k_b || !last_key || !ws) return CB_ERR_ARG;
+  if (ws_bytes < cb_analytics_workspace_size(m, cfg->n_q_heads, 0)) return CB_ERR_WORKSPACE;
+  return hip_status(launch_attention_deviation(cfg->dtype, m, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, q_a,
+                                               k_a, q_b, k_b, T, last_key, (double*)ws, out, (hipStream_t)stream));
+}
+
+extern "C" cb_status cb_spearman(const float* x, const float* y, int32_t n, double* out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  using namespace cb;
+  if (n <= 0 || !x || !y || !out || !ws) return CB_ERR_ARG;
+  if (ws_bytes < cb_analytics_workspace_size(0, 0, n)) return CB_ERR_WORKSPACE;
+  return hip_status(launch_spearman(x, y, n, (double*)ws, out, (hipStream_t)stream));
+}
+
+extern "C" cb_status cb_top_share(const float* x, int32_t n, int32_t k, double* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  using namespace cb;
+  if (n <= 0 || k < 0 || k > n || !x || !out || !ws) return CB_ERR_ARG;
+  if (ws_bytes < cb_analytics_workspace_size(0, 0, n)) return CB_ERR_WORKSPACE;
+  return hip_status(launch_top_share(x, n, k, (double*)ws, out, (hipStream_t)stream));
+}

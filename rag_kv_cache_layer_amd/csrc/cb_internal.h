@@ -341,6 +341,15 @@ int attn_key_split(int dtype, int m, int n_kv, int T);
 size_t attn_part_rows(int n_q, int n_kv);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
+// Deviation analytics (diagnostics): part >= m * n_q * 2 doubles, out device [2].
+hipError_t launch_attention_deviation(int dtype, int m, int n_q, int n_kv, int hd, const void* qa, const void* ka,
+                                      const void* qb, const void* kb, int T, const int* last_key, double* part,
+                                      double* out, hipStream_t s);
+// ranks >= 2n doubles; out device [1]
+hipError_t launch_spearman(const float* x, const float* y, int n, double* ranks, double* out, hipStream_t s);
+// contrib >= n doubles; out device [1]
+hipError_t launch_top_share(const float* x, int n, int k, double* contrib, double* out, hipStream_t s);
+
 // Streaming copy of bytes / 16 16-byte units (bytes % 16 == 0, both 16-byte aligned).
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

@@ -109,6 +109,11 @@ def lib() -> ctypes.CDLL:
         "cb_gemm_fp8": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P, SZ, P]),
         "cb_gemm_fp8_noalloc": (I32, [I32, I32, I32, P, P, P, P, P, I32, I32, P]),
         "cb_stream_copy": (I32, [P, P, SZ, P]),
+        "cb_workspace_q_offset": (SZ, [CFG, I32]),
+        "cb_analytics_workspace_size": (SZ, [I32, I32, I32]),
+        "cb_attention_deviation": (I32, [CFG, I32, P, P, P, P, I32, P, P, P, SZ, P]),
+        "cb_spearman": (I32, [P, P, I32, P, P, SZ, P]),
+        "cb_top_share": (I32, [P, I32, I32, P, P, SZ, P]),
         "cb_pick_ratio": (I32, [ctypes.c_double, ctypes.c_double, I32, ctypes.c_double, I32]),
         "cb_blend_stack": (I32, [CFG, I32, W, R, P, P, I64, P, P, I32, I32P, I32, I32, P, I32P, P, P, P, I32P, P, SZ,
                                  P, P]),
@@ -362,6 +367,66 @@ def rope_shift(cfg: LayerConfig, rope: DeviceRope, k_cache, layer_stride: int, n
                                _dptr(k_cache, "k_cache", torch_dtype(cfg), need), layer_stride, n_layers, T,
                                offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(offs) - 1,
                                _stream(stream)), "cb_rope_shift")
+
+
+def workspace_q(cfg: LayerConfig, ws, T: int, rows: int):
+    """View of the Q rows [rows][n_q][hd] that the last cb_blend_layer (with
+    this T) or cb_full_prefill_layer (over T rows) left in workspace ws
+    (cb_workspace_q_offset); valid until the next call on ws."""
+    torch = _torch()
+    off = int(lib().cb_workspace_q_offset(ctypes.byref(cfg), T))
+    if off == 0:
+        raise CacheBlendError(1, "cb_workspace_q_offset")
+    dt = torch_dtype(cfg)
+    es = torch.empty((), dtype=dt).element_size()
+    n = rows * cfg.n_q_heads * cfg.head_dim * es
+    return ws[off:off + n].view(dt).view(rows, cfg.n_q_heads, cfg.head_dim)
+
+
+def _analytics_ws(m: int, n_q: int, n: int, device):
+    torch = _torch()
+    return torch.empty(int(lib().cb_analytics_workspace_size(m, n_q, n)), dtype=torch.uint8, device=device)
+
+
+def attention_deviation(cfg: LayerConfig, q_a, k_a, q_b, k_b, last_key, stream=None):
+    """cb_attention_deviation: (||A_a - A_b||_F^2, ||A_b||_F^2) as Python floats."""
+    torch = _torch()
+    dt = torch_dtype(cfg)
+    m = q_a.shape[0]
+    T = k_a.shape[0]
+    kv = cfg.n_kv_heads * cfg.head_dim
+    qd = cfg.n_q_heads * cfg.head_dim
+    out = torch.empty(2, dtype=torch.float64, device=q_a.device)
+    ws = _analytics_ws(m, cfg.n_q_heads, 0, q_a.device)
+    _check(lib().cb_attention_deviation(ctypes.byref(cfg), m, _dptr(q_a, "q_a", dt, m * qd),
+                                        _dptr(k_a, "k_a", dt, T * kv), _dptr(q_b, "q_b", dt, m * qd),
+                                        _dptr(k_b, "k_b", dt, T * kv), T, _dptr(last_key, "last_key", torch.int32, m),
+                                        _dptr(out, "out"), _dptr(ws, "ws"), ws.numel(), _stream(stream)),
+           "cb_attention_deviation")
+    o = out.cpu()
+    return float(o[0]), float(o[1])
+
+
+def spearman(x, y, stream=None) -> float:
+    """cb_spearman of two device fp32 vectors."""
+    torch = _torch()
+    n = x.numel()
+    out = torch.empty(1, dtype=torch.float64, device=x.device)
+    ws = _analytics_ws(0, 0, n, x.device)
+    _check(lib().cb_spearman(_dptr(x, "x", torch.float32, n), _dptr(y, "y", torch.float32, n), n, _dptr(out, "out"),
+                             _dptr(ws, "ws"), ws.numel(), _stream(stream)), "cb_spearman")
+    return float(out.cpu()[0])
+
+
+def top_share(x, k: int, stream=None) -> float:
+    """cb_top_share: share of sum(x) held by its k largest values."""
+    torch = _torch()
+    n = x.numel()
+    out = torch.empty(1, dtype=torch.float64, device=x.device)
+    ws = _analytics_ws(0, 0, n, x.device)
+    _check(lib().cb_top_share(_dptr(x, "x", torch.float32, n), n, k, _dptr(out, "out"), _dptr(ws, "ws"), ws.numel(),
+                              _stream(stream)), "cb_top_share")
+    return float(out.cpu()[0])
 
 
 def stream_copy(src, dst, stream=None):

@@ -235,6 +235,25 @@ def test_gemm_fp8_noalloc_argument_errors(cblib):
     assert g(1100, 4096, 4096) == 4
 
 
+def test_analytics_argument_errors(cblib):
+    L, cfg = cblib, _cfg()
+    assert int(L.cb_workspace_q_offset(ctypes.byref(cfg), 100)) > 0
+    assert int(L.cb_workspace_q_offset(ctypes.byref(cfg), 0)) == 0
+    assert int(L.cb_workspace_q_offset(ctypes.byref(_cfg(n_q_heads=6, n_kv_heads=4)), 100)) == 0
+    need = int(L.cb_analytics_workspace_size(10, 8, 0))
+    assert need >= 10 * 8 * 2 * 8
+    ad = L.cb_attention_deviation
+    assert ad(ctypes.byref(cfg), -1, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, need, None) == 1
+    assert ad(ctypes.byref(cfg), 10, FAKE, None, FAKE, FAKE, 100, FAKE, FAKE, FAKE, need, None) == 1
+    assert ad(ctypes.byref(cfg), 10, FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, need - 1, None) == 4
+    assert ad(ctypes.byref(cfg), 0, None, None, None, None, 100, None, FAKE, None, 0, None) == 0
+    n_need = int(L.cb_analytics_workspace_size(0, 0, 50))
+    assert L.cb_spearman(FAKE, FAKE, 0, FAKE, FAKE, n_need, None) == 1
+    assert L.cb_spearman(FAKE, FAKE, 50, FAKE, FAKE, n_need - 1, None) == 4
+    assert L.cb_top_share(FAKE, 50, 51, FAKE, FAKE, n_need, None) == 1
+    assert L.cb_top_share(FAKE, 50, 5, FAKE, FAKE, n_need - 1, None) == 4
+
+
 def test_validate_switch(cblib):
     assert F.set_validate(True) is False
     assert F.set_validate(False) is True
