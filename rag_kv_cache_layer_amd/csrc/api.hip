@@ -456,7 +456,11 @@ extern "C" size_t cb_workspace_size(const cb_layer_config* cfg, int32_t T, int32
 }
 
 extern "C" const char* cb_status_string(cb_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the bits as an int, never as an
+  // out-of-range enumerator value
+  int32_t v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case CB_OK: return "ok";
     case CB_ERR_ARG: return "invalid argument";
     case CB_ERR_SHAPE: return "inconsistent shape";
