@@ -169,7 +169,7 @@ Ws layout(const cb_layer_config& c, int m, int T) {
   // attention key-split partials: only for row counts that use the split
   const size_t arows = std::min(M, attn_part_rows(c.n_q_heads, c.n_kv_heads));
   const size_t nsplit = c.dtype == CB_BF16 ? (size_t)(std::max(T, 1) + 511) / 512 : 0;
-  w.o_part = take(nsplit * arows * D.q_dim * 4);
+  w.o_part = take(nsplit * arows * D.q_dim * 2);   // bf16 partials
   w.ml_part = take(nsplit * arows * c.n_q_heads * 8);
   w.scratch = take(256);
   w.total = off;
@@ -735,7 +735,7 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
   aa.key_split = attn_key_split(dt, m_out, cfg->n_kv_heads, T);
-  aa.o_part = at<float>(ws, L.o_part);
+  aa.o_part = at<bf16_t>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
@@ -891,7 +891,7 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   aa.n_kv = cfg->n_kv_heads;
   aa.hd = D.hd;
   aa.key_split = attn_key_split(dt, T, cfg->n_kv_heads, T);
-  aa.o_part = at<float>(ws, L.o_part);
+  aa.o_part = at<bf16_t>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   st = hip_status(launch_attention(dt, aa, s));
   if (st) return st;
@@ -1350,7 +1350,7 @@ extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_w
   aa.n_kv = c.n_kv_heads;
   aa.hd = D.hd;
   aa.key_split = attn_key_split(dt, tiles * kAttnRowTile, c.n_kv_heads, T_max);
-  aa.o_part = at<float>(ws, L.o_part);
+  aa.o_part = at<bf16_t>(ws, L.o_part);
   aa.ml_part = at<float>(ws, L.ml_part);
   aa.req.n = n_req;
   int ro = 0, to = 0;

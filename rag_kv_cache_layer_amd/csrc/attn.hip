@@ -30,7 +30,8 @@
 //
 // When there are too few (row tile, KV head) workgroups to fill the chip, the
 // keys are split at fixed multiples of 512: each split writes an unnormalised
-// partial (O, running max, sum) and a merge kernel combines a row's splits in
+// partial (O rounded to bf16, which halves the partials' traffic; running max
+// and sum in fp32) and a merge kernel combines a row's splits in fp32 in
 // split order.  The split boundaries never depend on the other rows, so a row's
 // result still does not either.
 //
@@ -428,11 +429,13 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
     } else {
       // unnormalised partial of this key split, merged by attn_merge_kernel
       const int64_t slot = ((int64_t)split * a.m + i) * a.n_q + head;
-      float* Op = a.o_part + slot * HD + 4 * gp;
+      bf16_t* Op = a.o_part + slot * HD + 4 * gp;
 #pragma unroll
-      for (int mb = 0; mb < HD / 16; ++mb)
-        *reinterpret_cast<float4*>(Op + mb * 16) =
-            make_float4(oacc[b][mb][0], oacc[b][mb][1], oacc[b][mb][2], oacc[b][mb][3]);
+      for (int mb = 0; mb < HD / 16; ++mb) {
+        const uint32_t w0 = (uint32_t)f2bf(oacc[b][mb][0]) | ((uint32_t)f2bf(oacc[b][mb][1]) << 16);
+        const uint32_t w1 = (uint32_t)f2bf(oacc[b][mb][2]) | ((uint32_t)f2bf(oacc[b][mb][3]) << 16);
+        *reinterpret_cast<uint2*>(Op + mb * 16) = make_uint2(w0, w1);
+      }
       if (gp == 0) *reinterpret_cast<float2*>(a.ml_part + slot * 2) = make_float2(m_run[b], l_run[b]);
     }
   }
@@ -448,6 +451,13 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
 // always in bounds; values read for a tile that was not split are dropped).
 template <int HD>
 constexpr int merge_heads() { return 256 / (HD / 4); }
+
+// four consecutive bf16 partial values as fp32
+__device__ __forceinline__ float4 ld_bf16x4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
 constexpr int kMergeRegs = 8;   // splits a merge thread holds in registers at once
 
 template <int HD>
@@ -489,7 +499,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
         if (sp < ns) {
           const int64_t slot = slot0 + sp * stride;
           ml[sp] = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
-          o[sp] = *reinterpret_cast<const float4*>(a.o_part + slot * HD + c);
+          o[sp] = ld_bf16x4(a.o_part + slot * HD + c);
         }
       }
       float mx = -INFINITY;
@@ -512,7 +522,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       for (int sp = 0; sp < ns; ++sp) {
         const int64_t slot = slot0 + sp * stride;
         const float2 ml = *reinterpret_cast<const float2*>(a.ml_part + slot * 2);
-        const float4 o = *reinterpret_cast<const float4*>(a.o_part + slot * HD + c);
+        const float4 o = ld_bf16x4(a.o_part + slot * HD + c);
         const float wgt = exp2f(ml.x - mx);
         den += wgt * ml.y;
         num.x += wgt * o.x; num.y += wgt * o.y; num.z += wgt * o.z; num.w += wgt * o.w;

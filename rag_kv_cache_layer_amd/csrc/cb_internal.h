@@ -321,7 +321,7 @@ struct AttnArgs {
   void* O;                // [m][n_q*hd]
   int m, T, n_q, n_kv, hd;
   int key_split;          // 0: one pass over all keys; else keys split at multiples of this
-  float* o_part;          // [T / key_split][m][n_q][hd] unnormalised partials (key_split > 0)
+  bf16_t* o_part;         // [T / key_split][m][n_q][hd] unnormalised partials, bf16 (key_split > 0)
   float* ml_part;         // [T / key_split][m][n_q][2] running max (log2 units) and sum
   ReqTable req;           // several requests: row ranges, row tiles, K/V and T per request (T = max)
   // When a layer keeps every recomputed row, no selection kernel runs and the
