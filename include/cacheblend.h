@@ -89,7 +89,13 @@ typedef struct {
  * mlp_norm are fp32 [d_model].  w_gateup_packed is optional (NULL = unused):
  * W_gate and W_up repacked once by cb_pack_gateup, which the bf16 gate/up
  * projection then streams instead of w_gate and w_up (same results, bit for
- * bit). */
+ * bit).  w_qkv_folded is optional (NULL = unused): [W_q; W_k; W_v] with the
+ * attention RMSNorm gain folded in (cb_fold_qkv); with it the bf16 calls run
+ * the attention RMSNorm inside the QKV projection (the raw input rows are
+ * projected and each row's product is scaled by its 1 / rms, section 4.2's
+ * mask-then-project in one pass) instead of as a separate pass.  Results
+ * then differ from the unfolded path by rounding only (the normalised rows
+ * are not rounded to bf16 before the product; the folded weights are). */
 typedef struct {
   const void* attn_norm;
   const void* w_q;
@@ -101,6 +107,7 @@ typedef struct {
   const void* w_up;
   const void* w_down;
   const void* w_gateup_packed;
+  const void* w_qkv_folded;
 } cb_layer_weights;
 
 /* Device RoPE table: cos[p][hd/2], sin[p][hd/2] fp32 for p = 0 .. n_pos-1,
@@ -154,6 +161,14 @@ cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, int32_t r_las
 size_t cb_pack_gateup_size(const cb_layer_config* cfg);
 cb_status cb_pack_gateup(const cb_layer_config* cfg, const void* w_gate, const void* w_up,
                          void* packed, void* stream);
+
+/* One-time fold of the attention RMSNorm gain into the QKV weights (a
+ * model-load step): out[r][k] = W[r][k] * attn_norm[k] rounded to bf16 for
+ * the rows r of W_q, then W_k, then W_v (device, cb_fold_qkv_size(cfg)
+ * bytes, 16-byte aligned).  Reads w->w_q, w_k, w_v and attn_norm.
+ * CB_ERR_UNSUPPORTED for fp32 configs (cb_fold_qkv_size is then 0). */
+size_t cb_fold_qkv_size(const cb_layer_config* cfg);
+cb_status cb_fold_qkv(const cb_layer_config* cfg, const cb_layer_weights* w, void* out, void* stream);
 
 /* Bytes of device workspace needed by cb_blend_layer with up to m_max input
  * rows and by cb_full_prefill_layer with T <= m_max rows, and by

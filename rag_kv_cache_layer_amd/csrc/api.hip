@@ -195,6 +195,7 @@ cb_status check_weights(const cb_layer_weights* w) {
   for (const void* x : p)
     if (!x || !aligned16(x)) return CB_ERR_ARG;
   if (w->w_gateup_packed && !aligned16(w->w_gateup_packed)) return CB_ERR_ARG;
+  if (w->w_qkv_folded && !aligned16(w->w_qkv_folded)) return CB_ERR_ARG;
   return CB_OK;
 }
 
@@ -391,6 +392,26 @@ GemmArgs qkv_args(const cb_layer_config& c, const cb_layer_weights& w, const cb_
   g.splits = gemm_splits(c.dtype, gemm_n_tiles(c.dtype, g.B, g.N), g.K);
   g.part = at<float>(ws, L.part);
   return g;
+}
+
+// The QKV projection's input.  With a folded weight copy (bf16, no split-K)
+// the attention RMSNorm runs inside the projection: A is the raw rows
+// (gathered through in_rows) and every row's product is scaled by its
+// 1 / rms; otherwise a separate pass writes the normalised rows to xn.
+cb_status qkv_input(const cb_layer_config& c, const cb_layer_weights& w, GemmArgs& g, const void* hidden,
+                    int n_src, const int32_t* in_rows, int m, void* xn, bool allow_fold, hipStream_t s) {
+  if (allow_fold && c.dtype == CB_BF16 && w.w_qkv_folded && g.splits == 1) {
+    g.B.p0 = g.B.p1 = g.B.p2 = w.w_qkv_folded;
+    g.B.n1 = g.B.n2 = g.N;
+    g.A = hidden;
+    g.a_norm = 1;
+    g.a_rows = in_rows;
+    g.a_src_rows = n_src;
+    g.a_eps = c.rms_eps;
+    return CB_OK;
+  }
+  return hip_status(launch_rmsnorm(c.dtype, false, hidden, n_src, nullptr, in_rows, (const float*)w.attn_norm, xn, m,
+                                   c.d_model, c.rms_eps, s));
 }
 
 }  // namespace
@@ -658,7 +679,6 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
                     const void* hidden_in, const int32_t* in_rows, int k_out, void* hidden_out, float* dev_out,
                     int32_t* s_out, void* ws, hipStream_t s, const cb_layer_weights_fp8* w8 = nullptr) {
   const cb_layer_config* cfg = &c;
-  const cb_layer_weights* wp = &w;
   const int n_query = T - n_ctx;
   const int n_cand = m_in - n_query;
   const int m_out = std::min(k_out, n_cand) + n_query;
@@ -669,12 +689,10 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   const int n_src = in_rows ? T : m_in;
   cb_status st;
 
-  // 1. gather + attention RMSNorm
-  st = hip_status(launch_rmsnorm(dt, false, hidden_in, n_src, nullptr, in_rows, (const float*)wp->attn_norm,
-                                 at<void>(ws, L.xn), m_in, D.d, cfg->rms_eps, s));
-  if (st) return st;
-  // 2. QKV + RoPE + deviation + K/V scatter
+  // 1-2. gather + attention RMSNorm, QKV + RoPE + deviation + K/V scatter
   GemmArgs g = qkv_args(c, w, rope, L, ws, m_in);
+  st = qkv_input(c, w, g, hidden_in, n_src, in_rows, m_in, at<void>(ws, L.xn), w8 == nullptr, s);
+  if (st) return st;
   g.epi.rows = s_in;
   g.epi.pos0 = 0;
   g.epi.dev_lo = first_chunk_len;
@@ -868,10 +886,9 @@ extern "C" cb_status cb_full_prefill_layer(const cb_layer_config* cfg, const cb_
   const Ws L = layout(*cfg, T, T);
   hipStream_t s = (hipStream_t)stream;
   const int dt = cfg->dtype;
-  st = hip_status(launch_rmsnorm(dt, false, hidden_in, T, nullptr, nullptr, (const float*)w->attn_norm,
-                                 at<void>(ws, L.xn), T, D.d, cfg->rms_eps, s));
-  if (st) return st;
   GemmArgs g = qkv_args(*cfg, *w, *rope, L, ws, T);
+  st = qkv_input(*cfg, *w, g, hidden_in, T, nullptr, T, at<void>(ws, L.xn), true, s);
+  if (st) return st;
   g.epi.rows = nullptr;
   g.epi.pos0 = pos0;
   g.epi.k_cache = k_out;
@@ -1288,12 +1305,11 @@ extern "C" cb_status cb_blend_batch(const cb_layer_config* cfg, const cb_layer_w
   const Ws L = layout(c, std::max(T_max, M_in), T_max);
   hipStream_t s = (hipStream_t)stream;
   const int dt = c.dtype;
-  // 1. attention RMSNorm of every request's rows
-  st = hip_status(launch_rmsnorm(dt, false, hidden_in, M_in, nullptr, nullptr, (const float*)w->attn_norm,
-                                 at<void>(ws, L.xn), M_in, D.d, c.rms_eps, s));
-  if (st) return st;
-  // 2. one QKV GEMM over all rows; each row's epilogue uses its own request's cache
+  // 1-2. attention RMSNorm of every request's rows, one QKV GEMM over all
+  // rows; each row's epilogue uses its own request's cache
   GemmArgs g = qkv_args(c, *w, *rope, L, ws, M_in);
+  st = qkv_input(c, *w, g, hidden_in, M_in, nullptr, M_in, at<void>(ws, L.xn), true, s);
+  if (st) return st;
   g.epi.rows = s_in;
   g.epi.pos0 = 0;
   g.epi.k_cache = reqs[0].k_cache;
@@ -1541,4 +1557,24 @@ extern "C" cb_status cb_top_share(const float* x, int32_t n, int32_t k, double* 
   if (n <= 0 || k < 0 || k > n || !x || !out || !ws) return CB_ERR_ARG;
   if (ws_bytes < cb_analytics_workspace_size(0, 0, n)) return CB_ERR_WORKSPACE;
   return hip_status(launch_top_share(x, n, k, (double*)ws, out, (hipStream_t)stream));
+}
+
+extern "C" size_t cb_fold_qkv_size(const cb_layer_config* cfg) {
+  using namespace cb;
+  if (check_cfg(cfg) != CB_OK || cfg->dtype != CB_BF16) return 0;
+  const Dims D(*cfg);
+  return (size_t)D.n_qkv() * D.d * 2;
+}
+
+extern "C" cb_status cb_fold_qkv(const cb_layer_config* cfg, const cb_layer_weights* w, void* out, void* stream) {
+  using namespace cb;
+  cb_status st = check_cfg(cfg);
+  if (st) return st;
+  if (cfg->dtype != CB_BF16) return CB_ERR_UNSUPPORTED;
+  if (!w || !w->w_q || !w->w_k || !w->w_v || !w->attn_norm || !out || !aligned16(out) || !aligned16(w->w_q) ||
+      !aligned16(w->w_k) || !aligned16(w->w_v) || !aligned16(w->attn_norm))
+    return CB_ERR_ARG;
+  const Dims D(*cfg);
+  return hip_status(launch_fold_qkv(w->w_q, w->w_k, w->w_v, D.q_dim, D.kv_dim, D.d, (const float*)w->attn_norm, out,
+                                    (hipStream_t)stream));
 }

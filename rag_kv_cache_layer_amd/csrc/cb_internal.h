@@ -11,6 +11,7 @@ namespace cb {
 typedef uint16_t bf16_t;  // bf16 storage (upper half of an fp32)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -269,6 +270,14 @@ struct GemmArgs {
   EpiParams epi;
   int splits;             // split-K factor (bf16 only)
   float* part;            // [splits][M][n_tiles*BN] fp32 partials when splits > 1
+  // RMSNorm folded into the bf16 QKV projection (a_norm != 0, splits == 1):
+  // row i of A is row a_rows[i] (NULL = i) of an un-normalised [a_src_rows][K]
+  // buffer; the product of row i is scaled by 1 / sqrt(mean(A_i^2) + a_eps)
+  // before the epilogue (the RMSNorm gain is folded into B).
+  int a_norm;
+  const int* a_rows;
+  int a_src_rows;
+  float a_eps;
 };
 
 int gemm_bn(int dtype);                               // N tile width
@@ -349,6 +358,12 @@ hipError_t launch_attention_deviation(int dtype, int m, int n_q, int n_kv, int h
 hipError_t launch_spearman(const float* x, const float* y, int n, double* ranks, double* out, hipStream_t s);
 // contrib >= n doubles; out device [1]
 hipError_t launch_top_share(const float* x, int n, int k, double* contrib, double* out, hipStream_t s);
+
+// W_qkv [n_rows][K] bf16 = [W_q; W_k; W_v] with column k scaled by gain[k]
+// (rounded to bf16), the B operand of the QKV projection with the RMSNorm
+// folded in.
+hipError_t launch_fold_qkv(const void* w_q, const void* w_k, const void* w_v, int n_q_rows, int n_kv_rows, int K,
+                           const float* gain, void* out, hipStream_t s);
 
 // Streaming copy of bytes / 16 16-byte units (bytes % 16 == 0, both 16-byte aligned).
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

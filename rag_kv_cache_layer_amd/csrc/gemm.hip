@@ -154,7 +154,7 @@ __device__ void epi_store(const EpiParams& e, int gm, int c, const float v[8]) {
 // Apply the epilogue KIND to a bm x bn fp32 tile held in LDS (row stride cld).
 template <typename T, int bm, int bn, int NT, int KIND>
 __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float* Cs, int cld, int m0, int tn,
-                             int M, int N) {
+                             int M, int N, const float* row_scale = nullptr) {
   constexpr bool swiglu = KIND == EPI_SWIGLU;
   const int cols = swiglu ? bn / 2 : bn;
   const int tpr = cols / 8;  // threads per row (a power of two <= 64 for the QKV deviation reduction)
@@ -174,6 +174,11 @@ __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float*
       float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = row[lc + j];
+      if (row_scale) {
+        const float rs = row_scale[r];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] *= rs;
+      }
       if constexpr (swiglu) {
         const int f = tn * (bn / 2) + lc;
         if (f < B.n_feat) {
@@ -226,7 +231,8 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >>
 #endif
 constexpr int NSTAGE = CB_GEMM_NSTAGE;          // LDS ring depth (K steps in flight)
 constexpr int kStageBytes = (BM + BN) * BK * 2;  // 32 KB
-constexpr int kGemmSmem3 = NSTAGE * kStageBytes > BM * CLD * 4 ? NSTAGE * kStageBytes : BM * CLD * 4;
+// the ring, or the fp32 tile plus the folded RMSNorm's row scales
+constexpr int kGemmSmem3 = NSTAGE * kStageBytes > BM * CLD * 4 + BM * 4 ? NSTAGE * kStageBytes : BM * CLD * 4 + BM * 4;
 
 template <int KIND>
 __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmArgs g, int mt, int ntiles) {
@@ -247,7 +253,10 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
   // chunk slot ^ ((row >> 1) & 7).  Rows past the matrix and chunks past the
   // K range are out of the buffer's range and load as zero.
   const uint32_t kOOB = 0x80000000u;
-  __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
+  // folded RMSNorm (QKV only): A rows gathered from the un-normalised input
+  const bool fold = KIND == EPI_QKV && g.a_norm;
+  const int a_rows_total = fold ? g.a_src_rows : M;
+  __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, (uint32_t)((int64_t)a_rows_total * K * 2));
   __amdgpu_buffer_rsrc_t rb[4];
   uint32_t aoff[4], boff[4];
   int lcol[4];
@@ -257,7 +266,9 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     const int row = grp * 8 + (lane >> 3);
     const int slot = lane & 7;
     lcol[j] = (slot ^ ((row >> 1) & 7)) * 8;      // logical k offset of this lane's chunk
-    aoff[j] = m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB;
+    int src = m0 + row;
+    if (fold && src < M && g.a_rows) src = g.a_rows[src];
+    aoff[j] = (m0 + row < M && src >= 0 && src < a_rows_total) ? (uint32_t)((int64_t)src * K * 2) : kOOB;
     // B: the 8 rows of a group always come from one weight matrix
     const int r0 = grp * 8;
     const void* base;
@@ -300,6 +311,11 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   const int fr = lane & 15, fc = lane >> 4;
+  // folded RMSNorm: lane (fr, fc) of an even wave sums the squares of row
+  // wm + 16 i + fr over its k chunks (fc, fc + 4 of every step), from the
+  // fragments it already holds
+  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool do_ssq = fold && (w & 1) == 0;
 
   // one step's MFMAs; with CB_GEMM_ILV the next stage's DMA (nstage >= 0) is
   // issued one row group at a time between them
@@ -313,6 +329,15 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
       for (int i = 0; i < 4; ++i) {
         af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz(wm + i * 16 + fr, ks * 4 + fc));
         bfr[i] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn + i * 16 + fr, ks * 4 + fc));
+      }
+      if (do_ssq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2_t pr = {af[i][2 * e], af[i][2 * e + 1]};
+            ssq[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ssq[i], false);
+          }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -363,6 +388,19 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
   CB_WAIT_VMCNT(0);
   __syncthreads();
 
+  // folded RMSNorm: the row scales 1 / sqrt(mean(x^2) + eps) after the
+  // accumulator tile (the four lanes of a row add their sums in a fixed order)
+  float* rscale = (float*)(smem + BM * CLD * 4);
+  if (do_ssq) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float t = ssq[i];
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      if (fc == 0) rscale[wm + i * 16 + fr] = 1.0f / sqrtf(t / (float)K + g.a_eps);
+    }
+  }
+
   // accumulators -> fp32 tile in LDS.  Lane l of a 16x16 block holds column
   // l%16 and rows 4*(l/16) .. 4*(l/16)+3.
   float* Cs = (float*)smem;
@@ -387,7 +425,7 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     }
     return;
   }
-  run_epilogue<bf16_t, BM, BN, 256, KIND>(g.epi, g.B, Cs, CLD, m0, tn, M, g.N);
+  run_epilogue<bf16_t, BM, BN, 256, KIND>(g.epi, g.B, Cs, CLD, m0, tn, M, g.N, fold ? rscale : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -812,6 +850,41 @@ __global__ __launch_bounds__(256) void pack_gateup_kernel(const bf16_t* __restri
 }
 
 }  // namespace
+
+namespace {
+
+// one thread per 8 elements of a row of [W_q; W_k; W_v]
+__global__ __launch_bounds__(256) void fold_qkv_kernel(const bf16_t* __restrict__ wq, const bf16_t* __restrict__ wk,
+                                                       const bf16_t* __restrict__ wv, int n_q_rows, int n_kv_rows,
+                                                       int K, const float* __restrict__ gain, int64_t n_units,
+                                                       bf16_t* __restrict__ out) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= n_units) return;
+  const int upr = K / 8;
+  const int r = (int)(u / upr), c = (int)(u % upr) * 8;
+  const bf16_t* src = r < n_q_rows ? wq + (int64_t)r * K
+                      : r < n_q_rows + n_kv_rows ? wk + (int64_t)(r - n_q_rows) * K
+                                                 : wv + (int64_t)(r - n_q_rows - n_kv_rows) * K;
+  float v[8], gg[8];
+  load8(src + c, v);
+  load8(gain + c, gg);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] *= gg[j];
+  store8(out + (int64_t)r * K + c, v);
+}
+
+}  // namespace
+
+hipError_t launch_fold_qkv(const void* w_q, const void* w_k, const void* w_v, int n_q_rows, int n_kv_rows, int K,
+                           const float* gain, void* out, hipStream_t s) {
+  const int64_t n_units = (int64_t)(n_q_rows + 2 * n_kv_rows) * (K / 8);
+  if (n_units <= 0) return hipSuccess;
+  LaunchScope ls("fold_qkv", s);
+  fold_qkv_kernel<<<(unsigned)((n_units + 255) / 256), 256, 0, s>>>((const bf16_t*)w_q, (const bf16_t*)w_k,
+                                                                    (const bf16_t*)w_v, n_q_rows, n_kv_rows, K, gain,
+                                                                    n_units, (bf16_t*)out);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack_gateup(const void* w_gate, const void* w_up, int n_feat, int K, void* packed, hipStream_t s) {
   const int64_t n_chunks = (int64_t)(pack_gateup_bytes(n_feat, K) / 16);

@@ -45,7 +45,7 @@ class LayerConfig(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("attn_norm", "w_q", "w_k", "w_v", "w_o", "mlp_norm", "w_gate", "w_up", "w_down",
-                 "w_gateup_packed")]
+                 "w_gateup_packed", "w_qkv_folded")]
 
 
 class LayerWeightsFp8(ctypes.Structure):
@@ -123,6 +123,8 @@ def lib() -> ctypes.CDLL:
         "cb_workspace_size_fp8": (SZ, [CFG, I32, I32]),
         "cb_pack_gateup_size": (SZ, [CFG]),
         "cb_pack_gateup": (I32, [CFG, P, P, P, P]),
+        "cb_fold_qkv_size": (SZ, [CFG]),
+        "cb_fold_qkv": (I32, [CFG, W, P, P]),
         "cb_blend_layer_fp8": (I32, [CFG, ctypes.POINTER(LayerWeightsFp8), R, P, P, I32, I32, I32, P, I32, P, P, I32,
                                      P, P, P, I32P, P, SZ, P]),
     }
@@ -301,6 +303,20 @@ class DeviceLayer:
                                     _dptr(self.t["w_up"], "w_up"), _dptr(self.t["w_gateup_packed"], "packed"),
                                     _stream(stream)), "cb_pack_gateup")
         self.struct.w_gateup_packed = self.t["w_gateup_packed"].data_ptr()
+        return self
+
+    def fold_qkv(self, stream=None) -> "DeviceLayer":
+        """cb_fold_qkv: [W_q; W_k; W_v] with the attention RMSNorm gain folded
+        in, once; the layer's bf16 calls then run the RMSNorm inside the QKV
+        projection.  Returns self."""
+        torch = _torch()
+        n = int(lib().cb_fold_qkv_size(ctypes.byref(self.cfg)))
+        if n == 0:
+            raise CacheBlendError(5, "cb_fold_qkv_size")
+        self.t["w_qkv_folded"] = torch.empty(n, dtype=torch.uint8, device=self.t["w_q"].device)
+        _check(lib().cb_fold_qkv(ctypes.byref(self.cfg), ctypes.byref(self.struct),
+                                 _dptr(self.t["w_qkv_folded"], "out"), _stream(stream)), "cb_fold_qkv")
+        self.struct.w_qkv_folded = self.t["w_qkv_folded"].data_ptr()
         return self
 
 

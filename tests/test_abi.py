@@ -269,3 +269,17 @@ def test_pack_gateup_argument_errors(cblib):
     assert L.cb_pack_gateup(ctypes.byref(cfg), FAKE, FAKE, FAKE + 4, None) == 1
     w = F.LayerWeights(*([FAKE] * 9 + [FAKE + 2]))                               # misaligned packed copy
     assert _blend(L, cfg, w=w)[0] == 1
+
+
+def test_fold_qkv_argument_errors(cblib):
+    L, cfg = cblib, _cfg()
+    # [W_q; W_k; W_v] rows x d_model bf16
+    assert int(L.cb_fold_qkv_size(ctypes.byref(cfg))) == (512 + 2 * 128) * 512 * 2
+    assert int(L.cb_fold_qkv_size(ctypes.byref(_cfg(dtype="f32")))) == 0
+    w = F.LayerWeights(*([FAKE] * 9))
+    assert L.cb_fold_qkv(ctypes.byref(_cfg(dtype="f32")), ctypes.byref(w), FAKE, None) == 5
+    assert L.cb_fold_qkv(ctypes.byref(cfg), None, FAKE, None) == 1
+    assert L.cb_fold_qkv(ctypes.byref(cfg), ctypes.byref(w), FAKE + 8, None) == 1
+    assert L.cb_fold_qkv(ctypes.byref(cfg), ctypes.byref(F.LayerWeights(*([FAKE] * 3))), FAKE, None) == 1
+    wf = F.LayerWeights(*([FAKE] * 10 + [FAKE + 4]))                             # misaligned folded copy
+    assert _blend(L, cfg, w=wf)[0] == 1

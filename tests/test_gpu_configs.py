@@ -13,7 +13,8 @@
   (section 4.2: recomputing every token is the full prefill), so the GPU's
   result is compared with the oracle's full prefill on the same input.
 * The headline layer (6 x 512 + 32) with W_gate / W_up in the packed
-  streaming order the benchmark uses, against the oracle directly.
+  streaming order and the attention RMSNorm folded into the QKV projection,
+  as the benchmark runs it, against the oracle directly.
 
 Every case compares K/V on all rows (rows not recomputed bit-exact), the
 deviation of every candidate (per tensor and per element), the kept set
@@ -73,7 +74,7 @@ class _Gpu:
         self.cfg = F.config_of(p)
         self.layer = F.DeviceLayer(self.cfg, w)
         if packed:
-            self.layer.pack_gateup()
+            self.layer.pack_gateup().fold_qkv()
         self.rope = F.DeviceRope(self.cfg, T_max)
         self.ws = F.workspace(self.cfg, T_max, T_max)
         self.d = p.d_model

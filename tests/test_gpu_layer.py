@@ -30,14 +30,20 @@ CASES = [TINY, F32GQA, MED64, MED128, LONG]
 IDS = ["tiny_f32", "f32_gqa", "bf16_hd64", "bf16_hd128", "bf16_long"]
 
 
+# bf16 cases with the attention RMSNorm folded into the QKV projection
+FOLDED = [(p, f) for p, f in zip(CASES, IDS) if p.dtype == "bf16"]
+
+
 class Gpu:
     """Device copies of one single-layer case."""
 
-    def __init__(self, p, case):
+    def __init__(self, p, case, fold=False):
         self.p, self.c = p, case
         self.cfg = F.config_of(p)
         self.ad = act_dtype(p)
         self.layer = F.DeviceLayer(self.cfg, case["w"])
+        if fold:
+            self.layer.fold_qkv()   # attention RMSNorm inside the QKV projection
         self.rope = F.DeviceRope(self.cfg, p.T + 64)
         self.ws = F.workspace(self.cfg, p.T, p.T)
 
@@ -69,11 +75,12 @@ class Gpu:
         return host(k), host(v), host(y)
 
 
-@pytest.mark.parametrize("p", CASES, ids=IDS)
-def test_full_prefill(p):
+@pytest.mark.parametrize("p,fold", [(p, False) for p in CASES] + [(p, True) for p, _ in FOLDED],
+                         ids=IDS + [i + "_folded" for _, i in FOLDED])
+def test_full_prefill(p, fold):
     need_gpu()
     case = single_layer_case(p, 1, prepass_inputs=False)
-    g = Gpu(p, case)
+    g = Gpu(p, case, fold)
     x = case["hidden"]
     k, v, y = g.prefill(x)
     kw, vw, yw = layer.full_prefill(case["w"], x, p, 0, store=store_of(p))
@@ -85,14 +92,15 @@ def test_full_prefill(p):
     assert rel_err(k2, kw2) < tol and rel_err(y2, yw2) < tol
 
 
-@pytest.mark.parametrize("p", [TINY, MED64, LONG], ids=["tiny_f32", "bf16_hd64", "bf16_long"])
-def test_prefix_invariant_bit_exact(p):
+@pytest.mark.parametrize("p,fold", [(TINY, False), (MED64, False), (LONG, False), (MED64, True), (LONG, True)],
+                         ids=["tiny_f32", "bf16_hd64", "bf16_long", "bf16_hd64_folded", "bf16_long_folded"])
+def test_prefix_invariant_bit_exact(p, fold):
     """The first chunk's K/V and outputs from a prefill of that chunk alone
     equal those rows of the full-context prefill bit for bit (prefix caching:
     the prefix KV does not depend on what follows)."""
     need_gpu()
     case = single_layer_case(p, 2, prepass_inputs=False)
-    g = Gpu(p, case)
+    g = Gpu(p, case, fold)
     L0 = case["L0"]
     k, v, y = g.prefill(case["hidden"])
     k0, v0, y0 = g.prefill(case["hidden"][:L0])
@@ -117,14 +125,21 @@ def _check_blend(p, case, got, want, s_in, check_dev=True):
         assert rel_err(got["dev"][:n_cand], want["dev"][:n_cand]) < tol
 
 
-@pytest.mark.parametrize("p", CASES, ids=IDS)
-def test_select_then_blend_calls(p):
+@pytest.mark.parametrize("p,fold,gains", [(p, False, False) for p in CASES] +
+                         [(p, True, False) for p, _ in FOLDED] + [(MED64, True, True), (MED64, False, True)],
+                         ids=IDS + [i + "_folded" for _, i in FOLDED] + ["bf16_hd64_folded_gains", "bf16_hd64_gains"])
+def test_select_then_blend_calls(p, fold, gains):
     """The two calls of a single-layer workload: the select call recomputes
     every candidate and keeps the top k (section 4.3), the blend call
-    recomputes only the kept rows (section 4.2)."""
+    recomputes only the kept rows (section 4.2).  Also with the attention
+    RMSNorm folded into the QKV projection, and with RMSNorm gains other
+    than 1 (N(1, 0.2), seeded) so that the fold's gain scaling is exercised."""
     need_gpu()
     case = single_layer_case(p, 0)
-    g = Gpu(p, case)
+    if gains:
+        for name, seed in (("attn_norm", 61), ("mlp_norm", 62)):
+            case["w"][name] = (1.0 + 0.2 * np.random.default_rng(seed).standard_normal(p.d_model)).astype(np.float32)
+    g = Gpu(p, case, fold)
     st = store_of(p)
     T, n_ctx, L0 = p.T, p.n_ctx, case["L0"]
     k = blend.num_selected(p.r_e4, n_ctx, n_ctx - L0)
