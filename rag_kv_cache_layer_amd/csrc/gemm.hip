@@ -231,8 +231,9 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ ((r >>
 #endif
 constexpr int NSTAGE = CB_GEMM_NSTAGE;          // LDS ring depth (K steps in flight)
 constexpr int kStageBytes = (BM + BN) * BK * 2;  // 32 KB
-// the ring, or the fp32 tile plus the folded RMSNorm's row scales
-constexpr int kGemmSmem3 = NSTAGE * kStageBytes > BM * CLD * 4 + BM * 4 ? NSTAGE * kStageBytes : BM * CLD * 4 + BM * 4;
+// the ring, or the fp32 tile plus the folded RMSNorm's half sums and row scales
+constexpr int kGemmSmem3 =
+    NSTAGE * kStageBytes > BM * CLD * 4 + 3 * BM * 4 ? NSTAGE * kStageBytes : BM * CLD * 4 + 3 * BM * 4;
 
 template <int KIND>
 __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmArgs g, int mt, int ntiles) {
@@ -311,11 +312,15 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
   const int fr = lane & 15, fc = lane >> 4;
-  // folded RMSNorm: lane (fr, fc) of an even wave sums the squares of row
-  // wm + 16 i + fr over its k chunks (fc, fc + 4 of every step), from the
-  // fragments it already holds
-  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool do_ssq = fold && (w & 1) == 0;
+  // folded RMSNorm: the two waves that share rows wm .. wm+63 split the sum
+  // of squares of those rows: wave w adds, for the 32-deep half ks = w & 1 of
+  // every step, the Gram block A_i A_i^T of each of its 16-row fragments on
+  // the matrix cores (its diagonal holds the rows' sums of squares); the
+  // fragments are the ones the step's products already use
+  f32x4_t gram[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gram[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool do_ssq = fold;
 
   // one step's MFMAs; with CB_GEMM_ILV the next stage's DMA (nstage >= 0) is
   // issued one row group at a time between them
@@ -330,14 +335,9 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
         af[i] = *reinterpret_cast<const bf16x8_t*>(sa + swz(wm + i * 16 + fr, ks * 4 + fc));
         bfr[i] = *reinterpret_cast<const bf16x8_t*>(sb + swz(wn + i * 16 + fr, ks * 4 + fc));
       }
-      if (do_ssq) {
+      if (do_ssq && ks == (w & 1)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bf16x2_t pr = {af[i][2 * e], af[i][2 * e + 1]};
-            ssq[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ssq[i], false);
-          }
+        for (int i = 0; i < 4; ++i) gram[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], af[i], gram[i], 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -388,16 +388,17 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
   CB_WAIT_VMCNT(0);
   __syncthreads();
 
-  // folded RMSNorm: the row scales 1 / sqrt(mean(x^2) + eps) after the
-  // accumulator tile (the four lanes of a row add their sums in a fixed order)
-  float* rscale = (float*)(smem + BM * CLD * 4);
+  // folded RMSNorm: each wave's half of a row's sum of squares after the
+  // accumulator tile, then the row scales 1 / sqrt(mean(x^2) + eps) from the
+  // two halves in a fixed order
+  float* rhalf = (float*)(smem + BM * CLD * 4);   // [2][BM]
+  float* rscale = rhalf + 2 * BM;                  // [BM]
   if (do_ssq) {
+    // diagonal element (r, r) of a 16x16 block: lane r + 16 (r / 4), slot r % 4
+    const int r = fr;
+    if (lane == r + 16 * (r >> 2)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t = ssq[i];
-      t += __shfl_xor(t, 16);
-      t += __shfl_xor(t, 32);
-      if (fc == 0) rscale[wm + i * 16 + fr] = 1.0f / sqrtf(t / (float)K + g.a_eps);
+      for (int i = 0; i < 4; ++i) rhalf[(w & 1) * BM + wm + i * 16 + r] = gram[i][r & 3];
     }
   }
 
@@ -412,6 +413,10 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
       for (int v = 0; v < 4; ++v)
         Cs[(wm + i * 16 + fc * 4 + v) * CLD + wn + j * 16 + fr] = acc[i][j][v];
   __syncthreads();
+  if (fold) {
+    if (tid < BM) rscale[tid] = 1.0f / sqrtf((rhalf[tid] + rhalf[BM + tid]) / (float)K + g.a_eps);
+    __syncthreads();
+  }
 
   if (g.splits > 1) {
     // split-K partial; splitk_epilogue_kernel adds the splits in order
