@@ -8,10 +8,12 @@ embeddings N(0, 1) are seeded synthetic values; the cached K/V of each chunk
 come from an isolated prefill at position 0 and the hidden states from a full
 prefill of the same layer (set-up, untimed, on the GPU).
 
-One step is one fusor layer: the RoPE re-alignment of that layer's cached
-keys (cb_rope_shift) followed by the selective recompute of the HKVD rows
-(cb_blend_layer: gather + RMSNorm, QKV with RoPE, K deviation and K/V
-scatter, top-k, partial causal GQA attention, O projection, SwiGLU MLP).
+One step is one fusor layer in one call (cb_blend_layer_realign): the RoPE
+re-alignment of that layer's cached keys and the selective recompute of the
+HKVD rows (gather + RMSNorm, QKV with RoPE, K deviation and K/V scatter,
+top-k, partial causal GQA attention, O projection, SwiGLU MLP).  With
+--separate-shift the step is cb_rope_shift followed by cb_blend_layer (the
+same results, one launch more).
 value = context tokens blended per second = T / step time.
 
 Prints one JSON line.  --gpus above 1 is refused: the benchmark measures one GPU.
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--separate-shift", action="store_true",
+                    help="time cb_rope_shift + cb_blend_layer instead of the one-call cb_blend_layer_realign")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--extra", action="store_true", help="also time the select call and full prefill")
     ap.add_argument("--batch", type=int, default=0,
@@ -188,8 +192,11 @@ def main():
     vb = v_pre.clone()
 
     def step():
-        F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
-        F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, h_full, S, k, hout, dv, s_out, ws)
+        if args.separate_shift:
+            F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
+            F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, h_full, S, k, hout, dv, s_out, ws)
+        else:
+            F.blend_layer_realign(cfg, layer, rope, kb, vb, T, offs, S, m, h_full, S, k, hout, dv, s_out, ws)
 
     if args.calib_copy:
         src = torch.ones(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -371,7 +378,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) embeddings; cached KV from isolated prefill)",
         "config": {"workload": "llama8b_layer: 6x512-token chunks + 32-token query (T=3104), r=0.15, "
                                "k=461 HKVD + 32 query rows; d=4096, 32q/8kv heads x128, ffn 14336",
-                   "T": T, "k": k, "m": m, "step": "cb_rope_shift + cb_blend_layer",
+                   "T": T, "k": k, "m": m, "step": "cb_rope_shift + cb_blend_layer" if args.separate_shift else "cb_blend_layer_realign",
                    "weights": "bf16; W_gate/W_up repacked and the attention RMSNorm gain folded into W_qkv "
                               "once at load time (cb_pack_gateup, cb_fold_qkv; untimed)"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_BF16_TFLOPS,
@@ -520,10 +527,12 @@ def kdev_cold_measure(reps=6):
 def sweep_measure(seed, steps):
     """The 8B-shaped layer over n x 512 context tokens + 64 query tokens (chunk
     order permuted), n = 4, 16, 32, at recompute ratios r = 0.05 .. 1: for each
-    point the select call (untimed) picks S, then cb_rope_shift + the blend
-    call on S is timed, next to a full prefill of the same layer over all T
-    rows (the full KV recompute baseline).  Seeded N(0, 0.02) weights drawn
-    on the device, seeded N(0, 1) cached K/V and layer inputs."""
+    point the select call (untimed) picks S, then the step on S
+    (cb_blend_layer_realign: re-alignment + blend call) is timed, next to a
+    full prefill of the same layer over all T rows (the full KV recompute
+    baseline).  Seeded N(0, 0.02) weights drawn on the device (W_gate/W_up
+    packed and the attention RMSNorm folded into W_qkv, as for the 8B step),
+    seeded N(0, 1) cached K/V and layer inputs."""
     import torch
     from rag_kv_cache_layer_amd import fusor as F
     from rag_kv_cache_layer_amd import synth
@@ -538,7 +547,7 @@ def sweep_measure(seed, steps):
     w = {n: (torch.randn(s, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for n, s in shapes.items()}
     w["attn_norm"] = torch.ones(base.d_model, device="cuda")
     w["mlp_norm"] = torch.ones(base.d_model, device="cuda")
-    layer = F.DeviceLayer(cfg, w)
+    layer = F.DeviceLayer(cfg, w).pack_gateup().fold_qkv()
     del w
 
     def timed(fn, n):
@@ -579,8 +588,7 @@ def sweep_measure(seed, steps):
             kb, vb = k_pre.clone(), v_pre.clone()
 
             def step():
-                F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
-                F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, x, S, k, hout, dv, so, ws)
+                F.blend_layer_realign(cfg, layer, rope, kb, vb, T, offs, S, m, x, S, k, hout, dv, so, ws)
 
             ms = timed(step, steps)
             out.append({"chunks": n_chunks, "T": T, "r": r_e4 / 1e4, "k": k, "ms": round(ms, 4),
@@ -596,8 +604,8 @@ def layer70b_measure(seed, steps):
     """The blend call of one 70B-shaped layer (d 8192, 64/8 heads x 128, FFN
     28672; 8 x 500 + 32 tokens, r = 0.15) with seeded N(0, 0.02) weights drawn
     on the device, seeded N(0, 1) cached K/V and layer inputs: the select call
-    once (untimed) for the kept set, then cb_rope_shift + the blend call on
-    that set, as for the 8B layer."""
+    once (untimed) for the kept set, then the step on that set
+    (cb_blend_layer_realign, weights packed and folded), as for the 8B layer."""
     import torch
     from rag_kv_cache_layer_amd import fusor as F
     from rag_kv_cache_layer_amd import synth
@@ -611,7 +619,7 @@ def layer70b_measure(seed, steps):
     w = {n: (torch.randn(s, generator=g, device="cuda") * 0.02).to(torch.bfloat16) for n, s in shapes.items()}
     w["attn_norm"] = torch.ones(p.d_model, device="cuda")
     w["mlp_norm"] = torch.ones(p.d_model, device="cuda")
-    layer = F.DeviceLayer(cfg, w)
+    layer = F.DeviceLayer(cfg, w).pack_gateup().fold_qkv()
     del w
     T, n_ctx, kvd, d = p.T, p.n_ctx, p.kv_dim, p.d_model
     offs = synth.chunk_offsets(p, range(p.n_chunks))
@@ -635,8 +643,7 @@ def layer70b_measure(seed, steps):
     kb, vb = k_pre.clone(), v_pre.clone()
 
     def step():
-        F.rope_shift(cfg, rope, kb, T * kvd, 1, T, offs)
-        F.blend_layer(cfg, layer, rope, kb, vb, T, n_ctx, L0, S, m, x, S, k, hout, dv, so, ws)
+        F.blend_layer_realign(cfg, layer, rope, kb, vb, T, offs, S, m, x, S, k, hout, dv, so, ws)
 
     for _ in range(5):
         step()

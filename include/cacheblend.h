@@ -343,6 +343,32 @@ cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w,
                          int32_t k_out, void* hidden_out, float* dev_out, int32_t* s_out,
                          int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream);
 
+/* One layer of the fusor from a cache whose keys are still at their chunk-
+ * local positions: the re-alignment of cb_rope_shift (section 4.3, footnote
+ * 3) and the selective recompute of cb_blend_layer (section 4.2, Figure 5b)
+ * in one call.  The results -- cache, hidden_out, dev_out, s_out, m_out --
+ * are bit for bit those of cb_rope_shift(cfg, rope, k_cache, 0, 1, T,
+ * chunk_offsets, n_chunks, stream) followed by cb_blend_layer with n_ctx =
+ * chunk_offsets[n_chunks] and first_chunk_len = chunk_offsets[1] (n_ctx when
+ * n_chunks = 1).  Rows of chunks >= 1 that are not in s_in are re-aligned;
+ * rows in s_in get their new K/V (their deviation is taken against the
+ * re-aligned cached key).  On the bf16 path without split-K the
+ * re-alignment runs in the QKV projection's launch, on CUs the projection
+ * leaves idle; otherwise it is a launch of its own before the projection.
+ *  chunk_offsets: host int32 [n_chunks+1] as for cb_rope_shift (1 <=
+ *      n_chunks <= 256, CB_ERR_ARG for NULL or n_chunks < 1,
+ *      CB_ERR_UNSUPPORTED above 256, CB_ERR_SHAPE if not non-decreasing from
+ *      0 or chunk_offsets[n_chunks] > T).
+ *  Every other argument, its checks and the workspace are those of
+ *  cb_blend_layer.  The caller keeps ownership of every buffer. */
+cb_status cb_blend_layer_realign(const cb_layer_config* cfg, const cb_layer_weights* w,
+                                 const cb_rope_dev* rope, void* k_cache, void* v_cache, int32_t T,
+                                 const int32_t* chunk_offsets, int32_t n_chunks,
+                                 const int32_t* s_in, int32_t m_in, const void* hidden_in,
+                                 const int32_t* in_rows, int32_t k_out, void* hidden_out,
+                                 float* dev_out, int32_t* s_out, int32_t* m_out_host, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* The ordinary decoder layer over T rows at positions pos0 .. pos0+T-1 (the
  * "full KV recompute" baseline of section 7 and the isolated precompute of a
  * chunk at position 0).  hidden_in device [T][d]; k_out, v_out device

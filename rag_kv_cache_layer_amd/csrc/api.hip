@@ -677,7 +677,8 @@ namespace {
 cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const cb_rope_dev& rope, void* k_cache,
                     void* v_cache, int T, int n_ctx, int first_chunk_len, const int32_t* s_in, int m_in,
                     const void* hidden_in, const int32_t* in_rows, int k_out, void* hidden_out, float* dev_out,
-                    int32_t* s_out, void* ws, hipStream_t s, const cb_layer_weights_fp8* w8 = nullptr) {
+                    int32_t* s_out, void* ws, hipStream_t s, const cb_layer_weights_fp8* w8 = nullptr,
+                    const ShiftFuse* shift = nullptr) {
   const cb_layer_config* cfg = &c;
   const int n_query = T - n_ctx;
   const int n_cand = m_in - n_query;
@@ -701,6 +702,27 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
   g.epi.v_cache = v_cache;
   g.epi.T = T;
   g.epi.dev_part = at<float>(ws, L.devp);
+  if (shift) {
+    // the layer's re-alignment: inside the QKV launch where that kernel
+    // allows it, else as its own launch before the projection reads the cache
+    g.shift = shift;
+    if (w8 || !gemm_fuses_shift(dt, g)) {
+      g.shift = nullptr;
+      RopeShiftArgs ra{};
+      ra.k_cache = shift->k;
+      ra.layer_stride = 0;
+      ra.n_layers = 1;
+      ra.T = T;
+      ra.kv_dim = shift->kv_dim;
+      ra.hd = shift->hd;
+      ra.cos = shift->cos;
+      ra.sin = shift->sin;
+      ra.offsets = shift->offs.o;
+      ra.n_chunks = shift->n_chunks;
+      st = hip_status(launch_rope_shift(dt, ra, s));
+      if (st) return st;
+    }
+  }
   if (w8) {
     st = proj_fp8(g.A, m_in, D.d, w8->w_qkv, w8->e_qkv, D.n_qkv(), at<float>(ws, F8.prod), epilogue_ld(D.n_qkv()),
                   F8, ws, s, &g.part, &g.splits);
@@ -765,11 +787,15 @@ cb_status blend_run(const cb_layer_config& c, const cb_layer_weights& w, const c
 }  // namespace
 }  // namespace cb
 
-extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
-                                    void* k_cache, void* v_cache, int32_t T, int32_t n_ctx, int32_t first_chunk_len,
-                                    const int32_t* s_in, int32_t m_in, const void* hidden_in,
-                                    const int32_t* in_rows, int32_t k_out, void* hidden_out, float* dev_out,
-                                    int32_t* s_out, int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
+namespace cb {
+namespace {
+
+// Argument checks of a blend call (and validate mode); m_out on success.
+cb_status blend_checks(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
+                       void* k_cache, void* v_cache, int32_t T, int32_t n_ctx, int32_t first_chunk_len,
+                       const int32_t* s_in, int32_t m_in, const void* hidden_in, const int32_t* in_rows,
+                       int32_t k_out, void* hidden_out, int32_t* s_out, void* ws, size_t ws_bytes, void* stream,
+                       int* m_out) {
   cb_status st = check_cfg(cfg);
   if (st) return st;
   st = check_weights(w);
@@ -791,11 +817,72 @@ extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_w
     st = cb::validate_blend(s_in, m_in, in_rows, T, n_ctx, first_chunk_len, (hipStream_t)stream);
     if (st) return st;
   }
-  const int m_out = std::min(k_out, n_cand) + n_query;
+  *m_out = std::min(k_out, n_cand) + n_query;
+  return CB_OK;
+}
+
+}  // namespace
+}  // namespace cb
+
+extern "C" cb_status cb_blend_layer(const cb_layer_config* cfg, const cb_layer_weights* w, const cb_rope_dev* rope,
+                                    void* k_cache, void* v_cache, int32_t T, int32_t n_ctx, int32_t first_chunk_len,
+                                    const int32_t* s_in, int32_t m_in, const void* hidden_in,
+                                    const int32_t* in_rows, int32_t k_out, void* hidden_out, float* dev_out,
+                                    int32_t* s_out, int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
+  int m_out = 0;
+  const cb_status st = cb::blend_checks(cfg, w, rope, k_cache, v_cache, T, n_ctx, first_chunk_len, s_in, m_in,
+                                        hidden_in, in_rows, k_out, hidden_out, s_out, ws, ws_bytes, stream, &m_out);
+  if (st) return st;
   if (m_out_host) *m_out_host = m_out;
   if (m_in == 0) return CB_OK;
   return cb::blend_run(*cfg, *w, *rope, k_cache, v_cache, T, n_ctx, first_chunk_len, s_in, m_in, hidden_in, in_rows,
                        k_out, hidden_out, dev_out, s_out, ws, (hipStream_t)stream);
+}
+
+extern "C" cb_status cb_blend_layer_realign(const cb_layer_config* cfg, const cb_layer_weights* w,
+                                            const cb_rope_dev* rope, void* k_cache, void* v_cache, int32_t T,
+                                            const int32_t* chunk_offsets, int32_t n_chunks, const int32_t* s_in,
+                                            int32_t m_in, const void* hidden_in, const int32_t* in_rows,
+                                            int32_t k_out, void* hidden_out, float* dev_out, int32_t* s_out,
+                                            int32_t* m_out_host, void* ws, size_t ws_bytes, void* stream) {
+  if (!chunk_offsets || n_chunks < 1) return CB_ERR_ARG;
+  if (n_chunks > cb::kMaxChunks) return CB_ERR_UNSUPPORTED;
+  if (chunk_offsets[0] != 0) return CB_ERR_SHAPE;
+  for (int c = 0; c < n_chunks; ++c)
+    if (chunk_offsets[c + 1] < chunk_offsets[c]) return CB_ERR_SHAPE;
+  if (T < 0 || chunk_offsets[n_chunks] > T) return CB_ERR_SHAPE;
+  const int n_ctx = chunk_offsets[n_chunks];
+  const int first = n_chunks > 1 ? chunk_offsets[1] : n_ctx;
+  int m_out = 0;
+  cb_status st = cb::blend_checks(cfg, w, rope, k_cache, v_cache, T, n_ctx, first, s_in, m_in, hidden_in, in_rows,
+                                  k_out, hidden_out, s_out, ws, ws_bytes, stream, &m_out);
+  if (st) return st;
+  if (m_out_host) *m_out_host = m_out;
+  const Dims D(*cfg);
+  hipStream_t s = (hipStream_t)stream;
+  const bool shifts = n_chunks > 1 && n_ctx > first;
+  if (m_in == 0) {
+    // nothing recomputed: the re-alignment alone
+    if (!shifts) return CB_OK;
+    return cb_rope_shift(cfg, rope, k_cache, 0, 1, T, chunk_offsets, n_chunks, stream);
+  }
+  if (!shifts)
+    return cb::blend_run(*cfg, *w, *rope, k_cache, v_cache, T, n_ctx, first, s_in, m_in, hidden_in, in_rows, k_out,
+                         hidden_out, dev_out, s_out, ws, s);
+  cb::ShiftFuse sf{};
+  sf.row0 = first;
+  sf.row1 = n_ctx;
+  sf.n_chunks = n_chunks;
+  sf.kv_dim = D.kv_dim;
+  sf.hd = D.hd;
+  sf.k = k_cache;
+  sf.cos = rope->cos;
+  sf.sin = rope->sin;
+  sf.s_in = s_in;
+  sf.m_in = m_in;
+  for (int c = 0; c <= n_chunks; ++c) sf.offs.o[c] = chunk_offsets[c];
+  return cb::blend_run(*cfg, *w, *rope, k_cache, v_cache, T, n_ctx, first, s_in, m_in, hidden_in, in_rows, k_out,
+                       hidden_out, dev_out, s_out, ws, s, nullptr, &sf);
 }
 
 extern "C" size_t cb_pack_gateup_size(const cb_layer_config* cfg) {

@@ -148,6 +148,68 @@ struct RopeShiftArgs {
 };
 hipError_t launch_rope_shift(int dtype, const RopeShiftArgs& a, hipStream_t s);
 
+// Chunk offsets as kernel arguments (at most kMaxChunks chunks).
+constexpr int kMaxChunks = 256;
+struct ChunkOffsets {
+  int32_t o[kMaxChunks + 1];
+};
+
+// Re-alignment offset of cache row r >= o[1]: o[c] of the chunk c >= 1 that
+// holds it (the largest c in [1, n_chunks - 1] with o[c] <= r).
+__device__ __forceinline__ int chunk_delta(const ChunkOffsets& offs, int n_chunks, int r) {
+  int lo = 1, hi = n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs.o[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return offs.o[lo];
+}
+
+// The same offset found by a scan whose loads do not depend on r: with the
+// offsets in kernel arguments every load is uniform (scalar), so a thread
+// does not wait on a chain of dependent vector loads.
+__device__ __forceinline__ int chunk_delta_scan(const ChunkOffsets& offs, int n_chunks, int r) {
+  int delta = offs.o[1];
+  for (int c = 2; c < n_chunks; ++c) {
+    const int oc = offs.o[c];
+    delta = oc <= r ? oc : delta;
+  }
+  return delta;
+}
+
+// Rotation of 4 consecutive (even, odd) pairs by the angles whose cos / sin
+// are cs[0..3] / sn[0..3]: two rounded products and one rounded sum per
+// output, never contracted into fused multiply-adds, so every kernel that
+// re-aligns a key gets the same bits.
+__device__ __forceinline__ void rope_rotate8(const float v[8], const float* cs, const float* sn, float o[8]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = v[2 * j], b = v[2 * j + 1], c = cs[j], s = sn[j];
+    o[2 * j] = a * c - b * s;
+    o[2 * j + 1] = a * s + b * c;
+  }
+}
+
+// One layer's re-alignment run inside the launch of its QKV projection
+// (bf16, no split-K): the first n_wg workgroups of that launch rotate the
+// keys of rows [row0, row1) (chunks >= 1) that the call does not recompute
+// (not in s_in), and the projection's deviation epilogue compares each new
+// key with its cached key re-aligned in registers.  The cache then ends up
+// as after a separate cb_rope_shift followed by the layer, bit for bit.
+struct ShiftFuse {
+  int n_wg;
+  int row0, row1;
+  int n_chunks;
+  int kv_dim, hd;
+  void* k;                 // the layer's K cache [T][kv_dim]
+  const float* cos;        // [n_pos][hd / 2]
+  const float* sin;
+  const int32_t* s_in;     // rows the call recomputes (device)
+  int m_in;
+  ChunkOffsets offs;
+};
+
 // Expansion of 8-bit stored K/V (E4M3 codes, one power-of-two exponent per
 // (row, KV head)) into the cache, keys re-aligned when shift != 0.
 constexpr int kMaxShiftChunks = 256;
@@ -278,12 +340,18 @@ struct GemmArgs {
   const int* a_rows;
   int a_src_rows;
   float a_eps;
+  // host-side: when set (QKV, bf16, no split-K), launch_gemm runs the
+  // re-alignment it describes in the same launch
+  const ShiftFuse* shift;
 };
 
 int gemm_bn(int dtype);                               // N tile width
 int gemm_splits(int dtype, int N_tiles, int K);       // split-K choice (independent of M)
 int gemm_n_tiles(int dtype, const BOperand& B, int N);
 hipError_t launch_gemm(int dtype, const GemmArgs& g, hipStream_t s);
+// whether launch_gemm runs g.shift inside the launch (otherwise the caller
+// shifts first)
+bool gemm_fuses_shift(int dtype, const GemmArgs& g);
 // The epilogue of g.epi.kind (QKV, RESID or STORE; bf16 cache) applied to a
 // product already in g.part (g.splits fp32 slices of row stride
 // epilogue_ld(g.N)), e.g. one written by the fp8 GEMM.

@@ -33,6 +33,9 @@
 // thread): QKV (RoPE at each row's absolute position on Q and K, per-row K
 // deviation against the cached row before it is replaced, scatter of K/V into
 // the cache), residual add, and SwiGLU on interleaved gate/up tiles.
+#include <algorithm>
+#include <type_traits>
+
 #include "cb_internal.h"
 
 namespace cb {
@@ -75,8 +78,11 @@ __device__ __forceinline__ void rope8(float v[8], const float* cs, const float* 
 }
 
 // Q/K/V columns: returns this group's contribution to the row's K deviation.
+// With sf (re-alignment in the same launch) the cached key still sits at its
+// chunk-local position: it is rotated by its chunk's offset and rounded to
+// the cache type, exactly as the shift stores it, before the comparison.
 template <typename T>
-__device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8]) {
+__device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8], const ShiftFuse* sf) {
   const int crow = e.rows ? e.rows[gm] : gm;
   void* k_cache = e.k_cache;
   void* v_cache = e.v_cache;
@@ -109,6 +115,14 @@ __device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8]) {
     if (e.dev_part && crow >= dev_lo && crow < dev_hi) {
       float old[8];
       load8(kp, old);
+      if (sf) {
+        const int delta = chunk_delta_scan(sf->offs, sf->n_chunks, crow);
+        const int64_t t = (int64_t)delta * (e.hd / 2) + ((c - e.q_dim) % e.hd) / 2;
+        float rot[8];
+        rope_rotate8(old, sf->cos + t, sf->sin + t, rot);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) old[j] = Elem<T>::rnd(rot[j]);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float d = r[j] - old[j];
@@ -154,7 +168,7 @@ __device__ void epi_store(const EpiParams& e, int gm, int c, const float v[8]) {
 // Apply the epilogue KIND to a bm x bn fp32 tile held in LDS (row stride cld).
 template <typename T, int bm, int bn, int NT, int KIND>
 __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float* Cs, int cld, int m0, int tn,
-                             int M, int N, const float* row_scale = nullptr) {
+                             int M, int N, const float* row_scale = nullptr, const ShiftFuse* sf = nullptr) {
   constexpr bool swiglu = KIND == EPI_SWIGLU;
   const int cols = swiglu ? bn / 2 : bn;
   const int tpr = cols / 8;  // threads per row (a power of two <= 64 for the QKV deviation reduction)
@@ -190,7 +204,7 @@ __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float*
       } else {
         const int c = tn * bn + lc;
         if (c < N) {
-          if constexpr (KIND == EPI_QKV) contrib = epi_qkv<T>(e, gm, c, v);
+          if constexpr (KIND == EPI_QKV) contrib = epi_qkv<T>(e, gm, c, v, sf);
           else if constexpr (KIND == EPI_RESID) epi_resid<T>(e, gm, c, v);
           else epi_store<T>(e, gm, c, v);
         }
@@ -235,12 +249,71 @@ constexpr int kStageBytes = (BM + BN) * BK * 2;  // 32 KB
 constexpr int kGemmSmem3 =
     NSTAGE * kStageBytes > BM * CLD * 4 + 3 * BM * 4 ? NSTAGE * kStageBytes : BM * CLD * 4 + 3 * BM * 4;
 
-template <int KIND>
-__global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmArgs g, int mt, int ntiles) {
+// Re-alignment part of a fused QKV launch: workgroup b of sf.n_wg rotates
+// the keys of its share of rows [row0, row1) that are not in s_in, 16
+// elements per thread as rope_shift_kernel does (the same rotation and
+// rounding).  The recomputed rows are marked in LDS first: their keys are
+// replaced by the projection's epilogue in the same launch.
+__device__ __forceinline__ void shift_part(const ShiftFuse& sf, int b, char* smem) {
+  const int tid = threadIdx.x;
+  const int per = (sf.row1 - sf.row0 + sf.n_wg - 1) / sf.n_wg;
+  const int r_lo = sf.row0 + b * per, r_hi = min(sf.row1, r_lo + per);
+  if (r_lo >= r_hi) return;   // uniform over the workgroup
+  unsigned char* skip = (unsigned char*)smem;
+  for (int i = tid; i < r_hi - r_lo; i += 256) skip[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < sf.m_in; i += 256) {
+    const int r = sf.s_in[i];
+    if (r >= r_lo && r < r_hi) skip[r - r_lo] = 1;
+  }
+  __syncthreads();
+  const int upr = sf.kv_dim / 16;   // 16-element units per row
+  const int n_units = (r_hi - r_lo) * upr;
+  for (int u = tid; u < n_units; u += 256) {
+    const int rr = u / upr;
+    if (skip[rr]) continue;
+    const int r = r_lo + rr;
+    const int delta = chunk_delta_scan(sf.offs, sf.n_chunks, r);
+    bf16_t* p = (bf16_t*)sf.k + (int64_t)r * sf.kv_dim + (u % upr) * 16;
+    float v[2][8];
+    load8(p, v[0]);
+    load8(p + 8, v[1]);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int e = ((u % upr) * 16 + x * 8) % sf.hd;
+      const int64_t t = (int64_t)delta * (sf.hd / 2) + e / 2;
+      float o[8];
+      rope_rotate8(v[x], sf.cos + t, sf.sin + t, o);
+      store8(p + x * 8, o);
+    }
+  }
+}
+
+struct NoShift {};
+
+// 128x128 output tiles.  With SX = ShiftFuse (the QKV projection with the
+// layer's re-alignment in the same launch) the first sx.n_wg workgroups
+// shift keys, on CUs the projection's tiles leave idle, and the rest are
+// the projection's tiles.
+template <int KIND, typename SX>
+__global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmArgs g, int mt, int ntiles, SX sx) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmSmem3];
+  constexpr bool kShift = std::is_same<SX, ShiftFuse>::value;
+  static_assert(!kShift || KIND == EPI_QKV, "only the QKV projection re-aligns");
+  const ShiftFuse* sf = nullptr;
+  int bid = blockIdx.x, nblk = gridDim.x;
+  if constexpr (kShift) {
+    if (bid < sx.n_wg) {
+      shift_part(sx, bid, smem);
+      return;
+    }
+    bid -= sx.n_wg;
+    nblk -= sx.n_wg;
+    sf = &sx;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int id = xcd_remap(bid, nblk);
   const int tm = id % mt, tn = id / mt;
   const int m0 = tm * BM;
   const int M = g.M, K = g.K;
@@ -430,8 +503,9 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     }
     return;
   }
-  run_epilogue<bf16_t, BM, BN, 256, KIND>(g.epi, g.B, Cs, CLD, m0, tn, M, g.N, fold ? rscale : nullptr);
+  run_epilogue<bf16_t, BM, BN, 256, KIND>(g.epi, g.B, Cs, CLD, m0, tn, M, g.N, fold ? rscale : nullptr, sf);
 }
+
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel, large tile for the gate/up projection: 256 rows x LBN
@@ -682,7 +756,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, int nt
     } else {
       const int c = tn * BN + lc;
       if (c < g.N) {
-        if constexpr (KIND == EPI_QKV) contrib = epi_qkv<bf16_t>(e, gm, c, v);
+        if constexpr (KIND == EPI_QKV) contrib = epi_qkv<bf16_t>(e, gm, c, v, nullptr);
         else if constexpr (KIND == EPI_RESID) epi_resid<bf16_t>(e, gm, c, v);
         else epi_store<bf16_t>(e, gm, c, v);
       }
@@ -945,13 +1019,18 @@ hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g0, const float* ga
   const int mt = (g.M + BM - 1) / BM;
   {
     LaunchScope ls("gemm_o", s);
-    gemm_bf16_kernel<EPI_RESID><<<dim3(mt * ntiles, g.splits), 256, 0, s>>>(g, mt, ntiles);
+    gemm_bf16_kernel<EPI_RESID, NoShift><<<dim3(mt * ntiles, g.splits), 256, 0, s>>>(g, mt, ntiles, NoShift{});
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   LaunchScope ls("resid_norm", s);
   resid_norm_kernel<<<g.M, 256, 0, s>>>(g, ntiles, gain, eps, (bf16_t*)hn);
   return hipGetLastError();
+}
+
+bool gemm_fuses_shift(int dtype, const GemmArgs& g) {
+  return dtype == CB_BF16 && g.epi.kind == EPI_QKV && g.B.mode == 0 && g.splits <= 1 && g.epi.req.n == 0 &&
+         g.shift && g.shift->kv_dim % 16 == 0;
 }
 
 hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
@@ -974,13 +1053,23 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
     const dim3 grid(mt * ntiles, g.splits);
     const char* name = g.epi.kind == EPI_QKV ? "gemm_qkv" : g.epi.kind == EPI_SWIGLU ? "gemm_gateup"
                        : g.epi.kind == EPI_RESID && g.epi.out_f32 ? "gemm_o" : "gemm_down";
+    if (g.shift && gemm_fuses_shift(dtype, g)) {
+      // the layer's re-alignment on the CUs the projection's tiles leave idle
+      // (at least 32 workgroups, a multiple of 8 so the tiles keep their XCDs)
+      ShiftFuse sf = *g.shift;
+      const int tiles = mt * ntiles;
+      sf.n_wg = std::max(32, (256 - tiles % 256) / 8 * 8);
+      LaunchScope ls(name, s);
+      gemm_bf16_kernel<EPI_QKV, ShiftFuse><<<dim3(sf.n_wg + tiles), 256, 0, s>>>(g, mt, ntiles, sf);
+      return hipGetLastError();
+    }
     {
       LaunchScope ls(name, s);
       switch (g.epi.kind) {
-        case EPI_QKV: gemm_bf16_kernel<EPI_QKV><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
-        case EPI_RESID: gemm_bf16_kernel<EPI_RESID><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
-        case EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
-        default: gemm_bf16_kernel<EPI_STORE><<<grid, 256, 0, s>>>(g, mt, ntiles); break;
+        case EPI_QKV: gemm_bf16_kernel<EPI_QKV, NoShift><<<grid, 256, 0, s>>>(g, mt, ntiles, NoShift{}); break;
+        case EPI_RESID: gemm_bf16_kernel<EPI_RESID, NoShift><<<grid, 256, 0, s>>>(g, mt, ntiles, NoShift{}); break;
+        case EPI_SWIGLU: gemm_bf16_kernel<EPI_SWIGLU, NoShift><<<grid, 256, 0, s>>>(g, mt, ntiles, NoShift{}); break;
+        default: gemm_bf16_kernel<EPI_STORE, NoShift><<<grid, 256, 0, s>>>(g, mt, ntiles, NoShift{}); break;
       }
     }
     hipError_t e = hipGetLastError();

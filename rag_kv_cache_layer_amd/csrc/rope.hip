@@ -17,12 +17,6 @@ namespace cb {
 
 namespace {
 
-constexpr int kMaxChunks = 256;
-
-struct ChunkOffsets {
-  int32_t o[kMaxChunks + 1];
-};
-
 // 8-element units per thread: two (32 B in flight per thread) measure ~20%
 // faster than one on a cold stack-wide launch and match a plain copy within 7%.
 // A key row whose length is not a multiple of 8 * CB_ROPE_UPT elements (an
@@ -44,13 +38,7 @@ __global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int6
   int r = row0 + (int)(rr % n_rows);
   int l = (int)(rr / n_rows);
   const int cu0 = cu * UPT;   // this thread's first 8-element unit of the row
-  // chunk of row r: the largest c in [1, n_chunks-1] with o[c] <= r
-  int lo = 1, hi = n_chunks - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (offs.o[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  const int delta = offs.o[lo];
+  const int delta = chunk_delta(offs, n_chunks, r);
   T* p = k + (int64_t)l * lstride + (int64_t)r * kv_dim + cu0 * 8;
   float v[UPT][8];
 #pragma unroll
@@ -61,17 +49,7 @@ __global__ __launch_bounds__(256) void rope_shift_kernel(T* __restrict__ k, int6
     const float* cs = cosp + (int64_t)delta * (hd / 2) + e / 2;
     const float* sn = sinp + (int64_t)delta * (hd / 2) + e / 2;
     float o[8];
-    {
-      // two rounded products and one rounded sum per output: no contraction
-      // into fused multiply-adds in this block
-#pragma clang fp contract(off)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = v[x][2 * j], b = v[x][2 * j + 1], c = cs[j], s = sn[j];
-        o[2 * j] = a * c - b * s;
-        o[2 * j + 1] = a * s + b * c;
-      }
-    }
+    rope_rotate8(v[x], cs, sn, o);
     store8(p + x * 8, o);
   }
 }

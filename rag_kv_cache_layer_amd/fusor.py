@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         "cb_rope_shift": (I32, [CFG, R, P, I64, I32, I32, I32P, I32, P]),
         "cb_select_hkvd": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, SZ, P]),
         "cb_blend_layer": (I32, [CFG, W, R, P, P, I32, I32, I32, P, I32, P, P, I32, P, P, P, I32P, P, SZ, P]),
+        "cb_blend_layer_realign": (I32, [CFG, W, R, P, P, I32, I32P, I32, P, I32, P, P, I32, P, P, P, I32P, P, SZ,
+                                         P]),
         "cb_full_prefill_layer": (I32, [CFG, W, R, P, I32, I32, P, P, P, P, SZ, P]),
         "cb_blend_batch": (I32, [CFG, W, R, I32, ctypes.POINTER(BlendRequest), P, P, P, P, P, I32P, P, SZ, P]),
         "cb_stack_workspace_size": (SZ, [CFG, I32]),
@@ -481,6 +483,33 @@ def blend_layer(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, k_cache,
                                 _dptr(dev_out, "dev_out", torch.float32, m_in),
                                 _dptr(s_out, "s_out", torch.int32, m_exp), ctypes.byref(m_out),
                                 _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)), "cb_blend_layer")
+    return int(m_out.value)
+
+
+def blend_layer_realign(cfg: LayerConfig, layer: DeviceLayer, rope: DeviceRope, k_cache, v_cache, T: int,
+                        chunk_offsets: Sequence[int], s_in, m_in: int, hidden_in, in_rows, k_out: int, hidden_out,
+                        dev_out, s_out, ws, stream=None) -> int:
+    """cb_blend_layer_realign: the layer's RoPE re-alignment and one selective-
+    recompute layer in one call (k_cache still at chunk-local positions);
+    returns m_out."""
+    torch = _torch()
+    dt = torch_dtype(cfg)
+    kv, d = cfg.n_kv_heads * cfg.head_dim, cfg.d_model
+    offs = np.ascontiguousarray(np.asarray(chunk_offsets, dtype=np.int32))
+    n_ctx = int(offs[-1]) if len(offs) else 0
+    m_exp = max(expected_m_out(T, n_ctx, m_in, k_out), 0)
+    m_out = ctypes.c_int32(0)
+    _check(lib().cb_blend_layer_realign(ctypes.byref(cfg), ctypes.byref(layer.struct), ctypes.byref(rope.struct),
+                                        _dptr(k_cache, "k_cache", dt, T * kv), _dptr(v_cache, "v_cache", dt, T * kv),
+                                        T, offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(offs) - 1,
+                                        _dptr(s_in, "s_in", torch.int32, m_in), m_in,
+                                        _dptr(hidden_in, "hidden_in", dt, (T if in_rows is not None else m_in) * d),
+                                        _dptr(in_rows, "in_rows", torch.int32, m_in), k_out,
+                                        _dptr(hidden_out, "hidden_out", dt, m_exp * d),
+                                        _dptr(dev_out, "dev_out", torch.float32, m_in),
+                                        _dptr(s_out, "s_out", torch.int32, m_exp), ctypes.byref(m_out),
+                                        _dptr(ws, "ws", torch.uint8), ws.numel(), _stream(stream)),
+           "cb_blend_layer_realign")
     return int(m_out.value)
 
 

@@ -114,6 +114,39 @@ def test_blend_layer_argument_errors(cblib):
     assert st != 1 and st != 2
 
 
+def _realign(L, cfg, offs, n_chunks, **over):
+    args = dict(w=F.LayerWeights(*([FAKE] * 9)), rope=F.rope_dev(cfg, FAKE, FAKE, 4096), k=FAKE, v=FAKE, T=100,
+                s_in=FAKE, m_in=70, h_in=FAKE, in_rows=None, k_out=9, h_out=FAKE, dev=None, s_out=FAKE, ws=FAKE,
+                ws_bytes=1 << 40)
+    args.update(over)
+    m = ctypes.c_int32(-7)
+    st = L.cb_blend_layer_realign(ctypes.byref(cfg), ctypes.byref(args["w"]), ctypes.byref(args["rope"]),
+                                  args["k"], args["v"], args["T"], offs, n_chunks, args["s_in"], args["m_in"],
+                                  args["h_in"], args["in_rows"], args["k_out"], args["h_out"], args["dev"],
+                                  args["s_out"], ctypes.byref(m), args["ws"], args["ws_bytes"], None)
+    return st, m.value
+
+
+def test_blend_layer_realign_argument_errors(cblib):
+    """The offsets are checked as cb_rope_shift checks them, everything else
+    as cb_blend_layer does (n_ctx and the first chunk come from the offsets)."""
+    L, cfg = cblib, _cfg()
+    offs = (ctypes.c_int32 * 4)(0, 30, 60, 90)
+    assert _realign(L, cfg, None, 3)[0] == 1
+    assert _realign(L, cfg, offs, 0)[0] == 1
+    assert _realign(L, cfg, (ctypes.c_int32 * 4)(1, 30, 60, 90), 3)[0] == 2        # does not start at 0
+    assert _realign(L, cfg, (ctypes.c_int32 * 4)(0, 60, 30, 90), 3)[0] == 2        # decreasing
+    assert _realign(L, cfg, (ctypes.c_int32 * 4)(0, 30, 60, 101), 3)[0] == 2       # past T
+    assert _realign(L, cfg, (ctypes.c_int32 * 258)(*range(258)), 257, T=300)[0] == 5
+    assert _realign(L, cfg, offs, 3, k=None)[0] == 1
+    assert _realign(L, cfg, offs, 3, m_in=5)[0] == 2          # misses query rows
+    assert _realign(L, cfg, offs, 3, m_in=71)[0] == 2         # more rows than candidates after the first chunk
+    assert _realign(L, cfg, offs, 3, rope=F.rope_dev(cfg, FAKE, FAKE, 99))[0] == 2
+    assert _realign(L, cfg, offs, 3, rope=F.RopeDev(FAKE, FAKE, 4096, cfg.head_dim, 1e4))[0] == 1
+    st, m = _realign(L, cfg, offs, 3, ws_bytes=1000)
+    assert st == 4 and m == -7
+
+
 def test_other_calls_argument_errors(cblib):
     L, cfg = cblib, _cfg()
     offs = (ctypes.c_int32 * 3)(0, 40, 90)
