@@ -82,6 +82,32 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 constexpr int kKeySplit = CB_ATTN_SPLIT;   // smallest key split (multiple of kKeyTile)
 static_assert(kKeySplit % 64 == 0 && kKeySplit >= 512, "the partial buffers are sized for splits of >= 512 keys");
 
+// Lazy rescale threshold of the online softmax, in base-2 units of the
+// scores (0: the reference follows every new maximum)
+#ifndef CB_ATTN_TAU
+#define CB_ATTN_TAU 8
+#endif
+constexpr float kTau = CB_ATTN_TAU;
+
+// Maximum / sum over the four lane groups that hold one query's keys (lanes
+// q, q + 16, q + 32, q + 48) by the gfx950 row-swap permutes: after
+// permlane16_swap(x, x) the two results hold the values of rows 0 / 1 (and
+// 2 / 3) in every lane of those rows, after permlane32_swap those of the two
+// halves, so combining the pair reduces over the partners (in the same order
+// for every lane, up to the commutativity of the operation).
+__device__ __forceinline__ float max4g(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float sum4g(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
 // One wave instruction: 16 bytes per lane from the buffer at byte offset
 // `off` into LDS at lds + 16 * lane (loads past the buffer's end write zero).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
@@ -161,63 +187,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int head = kvh * G + w;
   const int q = lane & 15, gp = lane >> 4;
-  if (a.fin_ids_out && kvh == 0 && split == 0 && w == 0) {
-    // selection outputs of a layer that keeps every row (one wave per row tile)
-    for (int i = ti.r0 + lane; i < ti.r1; i += 64) {
-      a.fin_ids_out[i] = a.fin_ids_in[i];
-      float sdev;
-      if (i < a.fin_n_cand) {
-        sdev = 0.f;
-        for (int t = 0; t < a.fin_n_parts; ++t) sdev += a.fin_dev_part[(int64_t)t * a.fin_ld_part + i];
-      } else {
-        sdev = __builtin_nanf("");
-      }
-      a.fin_dev[i] = sdev;
-    }
-  }
-
-  int pos[2];
-  bool valid[2];
-  int pm = 0, pmin = INT_MAX;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int i = ti.r0 + b * 16 + q;
-    valid[b] = i < ti.r1;
-    int p = valid[b] ? (a.qpos ? a.qpos[i] : i) : 0;
-    pos[b] = p < 0 ? 0 : (p >= T_rows ? T_rows - 1 : p);
-    pm = max(pm, pos[b]);
-    if (valid[b]) pmin = min(pmin, pos[b]);
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    pm = max(pm, __shfl_xor(pm, o));
-    pmin = min(pmin, __shfl_xor(pmin, o));
-  }
-  // key range of this workgroup
-  const bool splitting = a.key_split > 0 && pm >= a.key_split;
-  const int k_lo = a.key_split > 0 ? split * a.key_split : 0;
-  const int k_hi = splitting ? min(pm + 1, k_lo + a.key_split) : pm + 1;
-  if (k_lo >= k_hi) return;   // uniform over the workgroup
-
-  const int ldq = a.n_q * HD, ldkv = a.n_kv * HD;
-  bf16x8_t qf[2][HD / 32];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int i = ti.r0 + b * 16 + q;
-    const int qr = valid[b] ? (a.qmap ? a.qmap[i] : i) : 0;
-    const gvec* Qp = (const gvec*)((const bf16_t*)a.Q + (int64_t)qr * ldq + head * HD + gp * 8);
-#pragma unroll
-    for (int ks = 0; ks < HD / 32; ++ks) {
-      u32x4_t u = valid[b] ? Qp[ks * 4] : u32x4_t{0u, 0u, 0u, 0u};
-      qf[b][ks] = __builtin_bit_cast(bf16x8_t, u);
-    }
-  }
-  f32x4_t oacc[2][HD / 16];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const int ldkv = a.n_kv * HD;
   // K/V of this KV head through buffer resources: rows at or past T lie
   // past the resource's end and load as zero (they are masked), and a
   // tile's row offset is a scalar operand
@@ -230,7 +200,6 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
   // natural [key][dim] layout, filled by direct-to-LDS loads: one wave
   // instruction fills a 1 KB block of RPB key rows; lane L fills 16-byte slot
   // L % CPR of row L / CPR with the dim chunk slot ^ f(row).
-  const int n_it = (k_hi - k_lo + KT - 1) / KT;
   uint32_t kof[KPW], vof[KPW];
 #pragma unroll
   for (int j = 0; j < KPW; ++j) {
@@ -251,6 +220,81 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
       dma16(rV, sv + blk * 1024, vof[j] + so);
     }
   };
+
+  // Q fragments of both 16-row blocks go out first (their addresses need no
+  // position), then the rows' positions and the first key tiles: the
+  // workgroup waits once for all of it
+  bool valid[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) valid[b] = ti.r0 + b * 16 + q < ti.r1;
+  const int ldq = a.n_q * HD;
+  bf16x8_t qf[2][HD / 32];
+  auto load_q = [&](const int (&qr)[2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const gvec* Qp = (const gvec*)((const bf16_t*)a.Q + (int64_t)qr[b] * ldq + head * HD + gp * 8);
+#pragma unroll
+      for (int ks = 0; ks < HD / 32; ++ks) {
+        u32x4_t u = valid[b] ? Qp[ks * 4] : u32x4_t{0u, 0u, 0u, 0u};
+        qf[b][ks] = __builtin_bit_cast(bf16x8_t, u);
+      }
+    }
+  };
+  // (two uniform paths, so that the common one, Q rows in row order, waits
+  // for no index load before issuing the fragment loads)
+  if (a.qmap) {
+    int qr[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) qr[b] = valid[b] ? a.qmap[ti.r0 + b * 16 + q] : 0;
+    load_q(qr);
+  } else {
+    int qr[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) qr[b] = valid[b] ? ti.r0 + b * 16 + q : 0;
+    load_q(qr);
+  }
+  int praw[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int i = ti.r0 + b * 16 + q;
+    praw[b] = valid[b] ? (a.qpos ? a.qpos[i] : i) : 0;
+  }
+  // the first NS-1 key tiles of the split go out while the Q fragments and
+  // positions are in flight: their start k_lo does not depend on the
+  // positions (tiles past the key range are never read; a workgroup with no
+  // keys waits for them before it ends)
+  const int k_lo = a.key_split > 0 ? split * a.key_split : 0;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) issue(st, k_lo + st * KT);
+  int pos[2];
+  int pm = 0, pmin = INT_MAX;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int p = praw[b];
+    pos[b] = p < 0 ? 0 : (p >= T_rows ? T_rows - 1 : p);
+    pm = max(pm, pos[b]);
+    if (valid[b]) pmin = min(pmin, pos[b]);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    pm = max(pm, __shfl_xor(pm, o));
+    pmin = min(pmin, __shfl_xor(pmin, o));
+  }
+  // key range of this workgroup
+  const bool splitting = a.key_split > 0 && pm >= a.key_split;
+  const int k_hi = splitting ? min(pm + 1, k_lo + a.key_split) : pm + 1;
+  if (k_lo >= k_hi) {   // uniform over the workgroup
+    CB_WAIT_VMCNT(0);
+    return;
+  }
+
+  f32x4_t oacc[2][HD / 16];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const int n_it = (k_hi - k_lo + KT - 1) / KT;
   // V^T operand reads: lane L = 16 g + 4 j + c4 points at the 4 dims
   // 16 mb + 4 c4 .. +3 of key 32 st + 4 g + j (+ 16 for the second read);
   // the transposing read hands lane 16 g + i the values of dim 16 mb + i for
@@ -258,9 +302,6 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
   const int tj = (lane >> 2) & 3, tc = lane & 3;
   const int tkey = 4 * gp + tj;                           // + 32 st (+ 16)
 
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < n_it) issue(st, k_lo + st * KT);
   for (int it0 = 0; it0 < n_it; it0 += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -332,17 +373,28 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
 #pragma unroll
         for (int kb = KB / 2; kb < KB; ++kb) mask_max(kb);
         // online softmax per query, in base-2 units (x = s * scale_log2, one
-        // fused multiply-add inside the exponent)
+        // fused multiply-add inside the exponent).  The reference maximum
+        // m_run moves only when the tile's maximum exceeds it by more than
+        // kTau (the exponents then stay below 2^kTau); the output and the sum
+        // are relative to the same reference, so the result is the softmax
+        // up to rounding, and a row's arithmetic depends on its own scores only
         bf16x8_t pb[2][KS];
         float alpha[2], m_use[2], sum[2] = {0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          float m = fmaxf(mx[b], __shfl_xor(mx[b], 16));
-          m = fmaxf(m, __shfl_xor(m, 32));
-          const float m_new = fmaxf(m_run[b], m * scale_log2);
-          m_use[b] = m_new == -INFINITY ? 0.f : m_new;   // a fully masked row stays empty
-          alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - m_use[b]);
-          m_run[b] = m_new;
+          const float mt = max4g(mx[b]) * scale_log2;
+          const bool grow = mt > m_run[b] + kTau;   // also the first keys of a row (m_run = -inf)
+          alpha[b] = grow ? __builtin_amdgcn_exp2f(m_run[b] - mt) : 1.f;
+          m_run[b] = grow ? mt : m_run[b];
+          m_use[b] = m_run[b] == -INFINITY ? 0.f : m_run[b];   // a fully masked row stays empty
+        }
+        // the output accumulators are rescaled only when some row's reference
+        // moved (a multiplication by exactly 1 for the others)
+        if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) != 0) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int mb = 0; mb < HD / 16; ++mb) oacc[b][mb] *= alpha[b];
         }
         // probabilities of the 32-key step st; P^T as the B operand: k slot j
         // of lane group gp is key 32st+4gp+j (j<4) or 32st+16+4gp+(j-4),
@@ -362,7 +414,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
         };
         // the output accumulators are rescaled by alpha (exactly 1 when the
         // running max did not grow) right before the P V product adds to them
-        auto pv = [&](int st, bool rescale) {
+        auto pv = [&](int st) {
 #pragma unroll
           for (int mb = 0; mb < HD / 16; ++mb) {
             const int c = 2 * mb + (tc >> 1), h8 = (tc & 1) * 8;
@@ -373,17 +425,13 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
                 (lds_v4s*)(sv + k2 * ROWB + ((c ^ fv(k2)) << 4) + h8));
             const bf16x8_t va =
                 __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            if (rescale) {
-              oacc[0][mb] *= alpha[0];
-              oacc[1][mb] *= alpha[1];
-            }
             oacc[0][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0][st], oacc[0][mb], 0, 0, 0);
             oacc[1][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[1][st], oacc[1][mb], 0, 0, 0);
           }
         };
         probs(0);
         __builtin_amdgcn_sched_barrier(0);
-        pv(0, true);
+        pv(0);
         probs(1);
         // first half's P V (transposing LDS reads + MFMAs, rescale) interleaved
         // with the second half's probabilities
@@ -394,14 +442,9 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
           __builtin_amdgcn_sched_group_barrier(0x002, CB_ATTN_SG_E, 0);   // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
-        pv(1, false);
+        pv(1);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          float t = sum[b];
-          t += __shfl_xor(t, 16);
-          t += __shfl_xor(t, 32);
-          l_run[b] = l_run[b] * alpha[b] + t;
-        }
+        for (int b = 0; b < 2; ++b) l_run[b] = l_run[b] * alpha[b] + sum4g(sum[b]);
       };
       // causal mask only on tiles that reach past some row's position
       // (uniform: every wave of the workgroup has the same rows)
@@ -410,6 +453,21 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
     }
   }
   CB_WAIT_VMCNT(0);
+  if (a.fin_ids_out && kvh == 0 && split == 0 && w == 0) {
+    // selection outputs of a layer that keeps every row (one wave per row
+    // tile, after its own attention work: nothing in the kernel reads them)
+    for (int i = ti.r0 + lane; i < ti.r1; i += 64) {
+      a.fin_ids_out[i] = a.fin_ids_in[i];
+      float sdev;
+      if (i < a.fin_n_cand) {
+        sdev = 0.f;
+        for (int t = 0; t < a.fin_n_parts; ++t) sdev += a.fin_dev_part[(int64_t)t * a.fin_ld_part + i];
+      } else {
+        sdev = __builtin_nanf("");
+      }
+      a.fin_dev[i] = sdev;
+    }
+  }
 
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
