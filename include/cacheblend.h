@@ -115,8 +115,8 @@ typedef struct {
  * head_dim and rope_theta name the configuration the table was built for;
  * every call that takes a table returns CB_ERR_ARG unless both equal the
  * call's cfg (a table of another base or head size would rotate by the
- * wrong angles), and CB_ERR_SHAPE when n_pos is below the positions the
- * call reads. */
+ * wrong angles) and cos and sin are 16-byte aligned, and CB_ERR_SHAPE when
+ * n_pos is below the positions the call reads. */
 typedef struct {
   const float* cos;
   const float* sin;

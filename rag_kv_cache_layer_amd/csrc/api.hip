@@ -182,7 +182,7 @@ T* at(void* ws, size_t off) {
 }
 
 cb_status check_rope(const cb_layer_config* c, const cb_rope_dev* r, int need) {
-  if (!r || !r->cos || !r->sin) return CB_ERR_ARG;
+  if (!r || !r->cos || !r->sin || !aligned16(r->cos) || !aligned16(r->sin)) return CB_ERR_ARG;
   // a table is only valid for the base and head size it was built with
   if (r->head_dim != c->head_dim || r->rope_theta != c->rope_theta) return CB_ERR_ARG;
   if (r->n_pos < need) return CB_ERR_SHAPE;

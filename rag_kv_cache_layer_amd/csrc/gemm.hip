@@ -69,12 +69,27 @@ __device__ __forceinline__ const T* b_row(const BOperand& B, int K, int N, int t
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ void rope8(float v[8], const float* cs, const float* sn) {
+  // two rounded products and one rounded sum per output, in every epilogue
+  // that applies it
+#pragma clang fp contract(off)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float a = v[2 * j], b = v[2 * j + 1];
     v[2 * j] = a * cs[j] - b * sn[j];
     v[2 * j + 1] = a * sn[j] + b * cs[j];
   }
+}
+
+// Sum of squared differences of 8 new and cached key values, added to acc in
+// element order with one fused multiply-add each (the same in every
+// epilogue that takes the deviation).
+__device__ __forceinline__ float dev_add8(const float r[8], const float old[8], float acc) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float d = r[j] - old[j];
+    acc = __builtin_fmaf(d, d, acc);
+  }
+  return acc;
 }
 
 // Q/K/V columns: returns this group's contribution to the row's K deviation.
@@ -123,11 +138,7 @@ __device__ float epi_qkv(const EpiParams& e, int gm, int c, float v[8], const Sh
 #pragma unroll
         for (int j = 0; j < 8; ++j) old[j] = Elem<T>::rnd(rot[j]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = r[j] - old[j];
-        contrib += d * d;
-      }
+      contrib = dev_add8(r, old, contrib);
     }
     store8(kp, r);
     return contrib;
@@ -165,10 +176,127 @@ __device__ void epi_store(const EpiParams& e, int gm, int c, const float v[8]) {
   else store8((T*)e.out + (int64_t)gm * e.ld_out + c, v);
 }
 
+// The QKV epilogue of a whole bm x bn tile for a single-request call, in
+// three phases so that a thread's memory reads for all of its rows are in
+// flight together: the rows' cache indices; then the RoPE table entries and
+// (deviation columns) the cached keys; then, row by row, the arithmetic and
+// the stores -- per element the same operations in the same order as
+// epi_qkv, so the results are identical.  RoPE tables are 16-byte aligned
+// (checked at the boundary), so a thread's four cos / sin entries are one
+// 16-byte load each.
+template <typename T, int bm, int bn, int NT>
+__device__ void qkv_tile_epilogue(const EpiParams& e, const float* Cs, int cld, int m0, int tn, int M, int N,
+                                  const float* row_scale, const ShiftFuse* sf) {
+  constexpr int tpr = bn / 8;           // threads per row (16 for 128 columns)
+  constexpr int rpp = NT / tpr;         // rows per pass
+  constexpr int NP = bm / rpp;          // passes
+  static_assert(NT % tpr == 0 && bm % rpp == 0, "whole passes");
+  const int tid = threadIdx.x;
+  const int lr = tid / tpr, lc = (tid % tpr) * 8;
+  const int c = tn * bn + lc;
+  const bool col_ok = c < N;
+  const bool is_q = c < e.q_dim;
+  const bool is_k = !is_q && c < e.q_dim + e.kv_dim;
+  const bool rope_col = c < e.q_dim + e.kv_dim;
+  const int dim = (is_q ? c : c - e.q_dim) % e.hd;
+  const bool k_tile = e.dev_part != nullptr && tn * bn < e.q_dim + e.kv_dim && tn * bn + bn > e.q_dim;
+  int crow[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int gm = m0 + p * rpp + lr;
+    int r = -1;
+    if (gm < M && col_ok) r = e.rows ? e.rows[gm] : gm;
+    crow[p] = (r >= 0 && r < e.T) ? r : -1;
+  }
+  float4 cs[NP], sn[NP], cd[NP], sd[NP];
+  uint4 oldk[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int r = crow[p];
+    if (r >= 0 && rope_col) {
+      const int64_t t = (int64_t)(r + e.pos0) * (e.hd / 2) + dim / 2;
+      cs[p] = *reinterpret_cast<const float4*>(e.cos + t);
+      sn[p] = *reinterpret_cast<const float4*>(e.sin + t);
+    }
+    if (r >= 0 && is_k && e.dev_part && r >= e.dev_lo && r < e.dev_hi) {
+      oldk[p] = *reinterpret_cast<const uint4*>((const T*)e.k_cache + (int64_t)r * e.kv_dim + (c - e.q_dim));
+      if (sf) {
+        const int delta = chunk_delta_scan(sf->offs, sf->n_chunks, r);
+        const int64_t t = (int64_t)delta * (e.hd / 2) + dim / 2;
+        cd[p] = *reinterpret_cast<const float4*>(sf->cos + t);
+        sd[p] = *reinterpret_cast<const float4*>(sf->sin + t);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int rl = p * rpp + lr;
+    const int gm = m0 + rl;
+    const int r = crow[p];
+    float contrib = 0.f;
+    if (r >= 0) {
+      const float* row = Cs + rl * cld;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = row[lc + j];
+      if (row_scale) {
+        const float rs = row_scale[rl];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] *= rs;
+      }
+      if (rope_col) {
+        const float ca[4] = {cs[p].x, cs[p].y, cs[p].z, cs[p].w};
+        const float sa[4] = {sn[p].x, sn[p].y, sn[p].z, sn[p].w};
+        rope8(v, ca, sa);
+      }
+      if (is_q) {
+        store8((T*)e.q_out + (int64_t)gm * e.q_dim + c, v);
+      } else if (is_k) {
+        T* kp = (T*)e.k_cache + (int64_t)r * e.kv_dim + (c - e.q_dim);
+        float rv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rv[j] = Elem<T>::rnd(v[j]);
+        if (e.dev_part && r >= e.dev_lo && r < e.dev_hi) {
+          float old[8];
+          const uint32_t wd[4] = {oldk[p].x, oldk[p].y, oldk[p].z, oldk[p].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            old[2 * j] = __uint_as_float(wd[j] << 16);
+            old[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
+          }
+          if (sf) {
+            const float ca[4] = {cd[p].x, cd[p].y, cd[p].z, cd[p].w};
+            const float sa[4] = {sd[p].x, sd[p].y, sd[p].z, sd[p].w};
+            float rot[8];
+            rope_rotate8(old, ca, sa, rot);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) old[j] = Elem<T>::rnd(rot[j]);
+          }
+          contrib = dev_add8(rv, old, contrib);
+        }
+        store8(kp, rv);
+      } else {
+        store8((T*)e.v_cache + (int64_t)r * e.kv_dim + (c - e.q_dim - e.kv_dim), v);
+      }
+    }
+    if (k_tile) {
+      // fixed-order reduction over the tpr consecutive lanes of this row
+      for (int o = tpr / 2; o > 0; o >>= 1) contrib += __shfl_xor(contrib, o);
+      if ((tid % tpr) == 0 && gm < M) e.dev_part[(int64_t)(tn - e.k_tile0) * M + gm] = contrib;
+    }
+  }
+}
+
 // Apply the epilogue KIND to a bm x bn fp32 tile held in LDS (row stride cld).
 template <typename T, int bm, int bn, int NT, int KIND>
 __device__ void run_epilogue(const EpiParams& e, const BOperand& B, const float* Cs, int cld, int m0, int tn,
                              int M, int N, const float* row_scale = nullptr, const ShiftFuse* sf = nullptr) {
+  if constexpr (KIND == EPI_QKV && std::is_same<T, bf16_t>::value && (NT % (bn / 8)) == 0) {
+    if (e.req.n == 0) {
+      qkv_tile_epilogue<T, bm, bn, NT>(e, Cs, cld, m0, tn, M, N, row_scale, sf);
+      return;
+    }
+  }
   constexpr bool swiglu = KIND == EPI_SWIGLU;
   const int cols = swiglu ? bn / 2 : bn;
   const int tpr = cols / 8;  // threads per row (a power of two <= 64 for the QKV deviation reduction)

@@ -195,6 +195,10 @@ def test_rope_table_must_match_config(cblib):
                                        FAKE, FAKE, FAKE, 1 << 40, None) == 1
         assert L.cb_kv_from_fp8(ctypes.byref(cfg), ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 1, 0, 100, FAKE, FAKE,
                                 0, 100, offs, 2, 1, None) == 1
+    # tables must be 16-byte aligned
+    misaligned = F.RopeDev(FAKE + 4, FAKE, 4096, cfg.head_dim, cfg.rope_theta)
+    assert _blend(L, cfg, rope=misaligned)[0] == 1
+    assert L.cb_rope_shift(ctypes.byref(cfg), ctypes.byref(misaligned), FAKE, 0, 1, 100, offs, 2, None) == 1
     # the same table with matching fields passes the check (and fails later, on the workspace)
     assert L.cb_full_prefill_layer(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(good), FAKE, 100, 0, FAKE,
                                    FAKE, FAKE, FAKE, 16, None) == 4
