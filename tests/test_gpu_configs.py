@@ -31,7 +31,7 @@ import functools
 import numpy as np
 import pytest
 
-from oracle import blend, layer
+from oracle import blend, layer, rope
 from oracle.storage import round_store
 from rag_kv_cache_layer_amd import fusor as F
 from rag_kv_cache_layer_amd import synth
@@ -79,7 +79,10 @@ class _Gpu:
         self.ws = F.workspace(self.cfg, T_max, T_max)
         self.d = p.d_model
 
-    def blend(self, c, s_in, k_out):
+    def blend(self, c, s_in, k_out, mode="plain"):
+        """mode: "plain" (cb_blend_layer on c's cache), "realign" (c's keys at
+        chunk-local positions, cb_blend_layer_realign) or "two" (the same
+        keys, cb_rope_shift then cb_blend_layer)."""
         T, n_ctx = c["T"], c["n_ctx"]
         kc, vc = dev(c["k"], torch.bfloat16), dev(c["v"], torch.bfloat16)
         x = dev(c["x"], torch.bfloat16)
@@ -89,8 +92,15 @@ class _Gpu:
         dv = torch.empty(m_in, dtype=torch.float32, device="cuda")
         so = torch.empty(m_out, dtype=torch.int32, device="cuda")
         s_t = dev(np.asarray(s_in, np.int32), torch.int32)
-        got_m = F.blend_layer(self.cfg, self.layer, self.rope, kc, vc, T, n_ctx, c["L0"], s_t, m_in, x, s_t, k_out,
-                              hout, dv, so, self.ws)
+        offs = [int(o) for o in c["offs"]]
+        if mode == "realign":
+            got_m = F.blend_layer_realign(self.cfg, self.layer, self.rope, kc, vc, T, offs, s_t, m_in, x, s_t, k_out,
+                                          hout, dv, so, self.ws)
+        else:
+            if mode == "two":
+                F.rope_shift(self.cfg, self.rope, kc, 0, 1, T, offs)
+            got_m = F.blend_layer(self.cfg, self.layer, self.rope, kc, vc, T, n_ctx, c["L0"], s_t, m_in, x, s_t,
+                                  k_out, hout, dv, so, self.ws)
         assert got_m == m_out
         torch.cuda.synchronize()
         return dict(k=host(kc), v=host(vc), y=host(hout), dev=host(dv), s_out=so.cpu().numpy())
@@ -152,11 +162,12 @@ def _compare(got, ora, c, rows, want_y):
     assert rel_err(got["y"][rows], want_y) < TOL
 
 
-def _blend_case(p, w, gpu, c, s_in, k_out, name, sample=48):
+def _blend_case(p, w, gpu, c, s_in, k_out, name, sample=48, c_gpu=None, mode="plain"):
     """The GPU blend call against the oracle on one (S_in, k_out); returns the
-    GPU's kept set."""
+    GPU's kept set.  c_gpu: the GPU call's inputs when they differ from the
+    oracle's (keys at chunk-local positions for mode "realign")."""
     ora = _Oracle(p, w, c, s_in)
-    got = gpu.blend(c, s_in, k_out)
+    got = gpu.blend(c if c_gpu is None else c_gpu, s_in, k_out, mode)
     n_cand = len(ora.cand)
     k_eff = min(k_out, n_cand)
     keep = blend.topk_hkvd(got["dev"][:n_cand], k_eff)
@@ -291,3 +302,26 @@ def test_llama8b_layer_packed_gateup():
     k = F.num_selected(p.r_e4, n_ctx, n_ctx - L0)
     S = _blend_case(p, w, gpu, c, np.arange(L0, T), k, "8B layer packed select call", sample=96)
     _blend_case(p, w, gpu, c, S, k, "8B layer packed blend call", sample=None)
+
+
+def test_llama8b_layer_realign():
+    """The benchmark's call at full size: cb_blend_layer_realign from a cache
+    whose keys are at their chunk-local positions (the seeded keys of the
+    case), packed and folded weights.  The oracle re-aligns the same keys
+    (oracle.rope.rope_shift) and runs its select and blend calls; the blend
+    call also equals cb_rope_shift + cb_blend_layer bit for bit."""
+    need_gpu()
+    p = synth.PRESETS["llama8b_layer"]
+    w = synth.layer_weights(p, 3, 0)
+    c = _case_inputs(p, 3, w)
+    c_ora = dict(c, k=rope.rope_shift(c["k"], c["offs"], p.rope_theta, "bf16"))
+    gpu = _Gpu(p, w, p.T, packed=True)
+    n_ctx, L0, T = p.n_ctx, c["L0"], p.T
+    k = F.num_selected(p.r_e4, n_ctx, n_ctx - L0)
+    S = _blend_case(p, w, gpu, c_ora, np.arange(L0, T), k, "8B layer realign select call", sample=96, c_gpu=c,
+                    mode="realign")
+    _blend_case(p, w, gpu, c_ora, S, k, "8B layer realign blend call", sample=None, c_gpu=c, mode="realign")
+    a, b = gpu.blend(c, S, k, "realign"), gpu.blend(c, S, k, "two")
+    for key in ("k", "v", "y", "s_out"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["dev"], b["dev"], equal_nan=True)
