@@ -72,6 +72,16 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 #ifndef CB_ATTN_SG_E
 #define CB_ATTN_SG_E 8
 #endif
+// wave priority raised over the MFMA-dense parts of a tile (the scores, the
+// P V products), so that the SIMD's other wave fills the matrix pipe's gaps
+// with its vector work rather than competing for issue
+#ifndef CB_ATTN_PRIO
+#define CB_ATTN_PRIO 1
+#endif
+#define CB_PRIO(n)                                  \
+  do {                                              \
+    if constexpr (CB_ATTN_PRIO) __builtin_amdgcn_s_setprio(n); \
+  } while (0)
 // workgroups the key split aims at when the (row tile, KV head) grid is small
 #ifndef CB_ATTN_WG_TARGET
 #define CB_ATTN_WG_TARGET 768
@@ -354,6 +364,7 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
               mx[b] = fmaxf(mx[b], s[b][kb][v]);
             }
         };
+        CB_PRIO(1);
 #pragma unroll
         for (int kb = 0; kb < KB / 2; ++kb) scores(kb);
         __builtin_amdgcn_sched_barrier(0);
@@ -363,15 +374,19 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
         for (int kb = 0; kb < KB / 2; ++kb) mask_max(kb);
         // second half's scores (K fragment reads + MFMAs) interleaved with the
         // first half's mask and max
+        // (all of the half's K fragment reads go first, so that each MFMA pair
+        // waits only for its own fragment, not for a read issued just before)
+        constexpr int NB = (KB / 2) * (HD / 32);   // K fragment reads, one per MFMA pair
+        __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);   // LDS reads
 #pragma unroll
-        for (int i = 0; i < (KB / 2) * (HD / 32); ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        for (int i = 0; i < NB; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, CB_ATTN_SG_B, 0);   // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = KB / 2; kb < KB; ++kb) mask_max(kb);
+        CB_PRIO(0);
         // online softmax per query, in base-2 units (x = s * scale_log2, one
         // fused multiply-add inside the exponent).  The reference maximum
         // m_run moves only when the tile's maximum exceeds it by more than
@@ -431,18 +446,22 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
         };
         probs(0);
         __builtin_amdgcn_sched_barrier(0);
+        CB_PRIO(1);
         pv(0);
         probs(1);
         // first half's P V (transposing LDS reads + MFMAs, rescale) interleaved
         // with the second half's probabilities
+        // (all transposing reads of the half first, as for the scores)
+        constexpr int NP = HD / 16;   // V^T fragment read pairs, one per MFMA pair
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NP, 0);   // LDS reads
 #pragma unroll
-        for (int i = 0; i < HD / 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read
+        for (int i = 0; i < NP; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, CB_ATTN_SG_E, 0);   // VALU
         }
         __builtin_amdgcn_sched_barrier(0);
         pv(1);
+        CB_PRIO(0);
 #pragma unroll
         for (int b = 0; b < 2; ++b) l_run[b] = l_run[b] * alpha[b] + sum4g(sum[b]);
       };
