@@ -70,11 +70,15 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 #define CB_ATTN_SG_B 3
 #endif
 #ifndef CB_ATTN_SG_E
-#define CB_ATTN_SG_E 8
+#define CB_ATTN_SG_E 4
 #endif
 // wave priority raised over the MFMA-dense parts of a tile (the scores, the
 // P V products), so that the SIMD's other wave fills the matrix pipe's gaps
 // with its vector work rather than competing for issue
+// the first half's K fragment reads also all before its MFMAs
+#ifndef CB_ATTN_FH
+#define CB_ATTN_FH 1
+#endif
 #ifndef CB_ATTN_PRIO
 #define CB_ATTN_PRIO 1
 #endif
@@ -367,6 +371,10 @@ __global__ __launch_bounds__(64 * G, G >= 2 ? CB_ATTN_MINB : 1) void attn_bf16_k
         CB_PRIO(1);
 #pragma unroll
         for (int kb = 0; kb < KB / 2; ++kb) scores(kb);
+#if CB_ATTN_FH
+        __builtin_amdgcn_sched_group_barrier(0x100, (KB / 2) * (HD / 32), 0);   // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, KB * (HD / 32), 0);         // MFMA
+#endif
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = KB / 2; kb < KB; ++kb) scores(kb);
