@@ -163,7 +163,7 @@ Ws layout(const cb_layer_config& c, int m, int T) {
   w.sel = take(M * 4);
   w.o = take(M * D.q_dim * D.b);
   w.h = take(M * D.d * 4);
-  w.hn = take(M * D.d * D.b);
+  w.hn = take((size_t)act_packed_rows((int)M) * D.d * D.b);   // row-major or step-major (gate/up input)
   w.u = take(M * D.F * D.b);
   w.part = take(part_floats(c.dtype, D, (int)M) * 4);
   // attention key-split partials: only for row counts that use the split
@@ -307,7 +307,9 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   g.epi.ld_out = D.d;
   g.splits = gemm_splits(dt, gemm_n_tiles(dt, g.B, g.N), g.K);
   g.part = at<float>(ws, L.part);
-  // ... and RMSNorm(h) -> hn
+  // ... and RMSNorm(h) -> hn, in the step-major layout when the bf16
+  // gate/up projection reads it so
+  const bool hn_packed = !w8 && gemm_gateup_packed_a(dt, D.d);
   cb_status st;
   if (w8) {
     st = proj_fp8(g.A, m_out, D.q_dim, w8->w_o, w8->e_o, D.d, at<float>(ws, F8->prod), epilogue_ld(D.d), *F8, ws,
@@ -315,7 +317,8 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
     if (st) return st;
     st = hip_status(launch_resid_norm_only(g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s));
   } else {
-    st = hip_status(launch_gemm_resid_norm(dt, g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s));
+    st = hip_status(
+        launch_gemm_resid_norm(dt, g, (const float*)w.mlp_norm, c.rms_eps, at<void>(ws, L.hn), s, hn_packed));
   }
   if (st) return st;
   // gate/up + SwiGLU -> u
@@ -329,6 +332,7 @@ cb_status layer_tail(const cb_layer_config& c, const cb_layer_weights& w, const 
   gu.B.p2 = w.w_up;
   gu.B.n_feat = D.F;
   gu.B.packed = dt == CB_BF16 ? w.w_gateup_packed : nullptr;
+  gu.a_packed = hn_packed ? 1 : 0;
   gu.epi.kind = EPI_SWIGLU;
   gu.epi.out = at<void>(ws, L.u);
   gu.epi.ld_out = D.F;

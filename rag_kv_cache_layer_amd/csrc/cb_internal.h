@@ -237,8 +237,11 @@ hipError_t launch_kv_expand(int dtype, const KvExpandArgs& a, const int32_t* off
 // out[i] = start + i for i < n (the row list of a stack's first layer)
 hipError_t launch_iota(int* out, int n, int start, hipStream_t s);
 
+// packed_out: write the rows in the step-major layout of act_packed_index
+// (bf16 output, d a multiple of 32)
 hipError_t launch_rmsnorm(int dtype, bool x_f32, const void* x, int n_src, const int* m1, const int* m2,
-                          const float* g, void* out, int rows, int d, float eps, hipStream_t s);
+                          const float* g, void* out, int rows, int d, float eps, hipStream_t s,
+                          bool packed_out = false);
 
 // Deviation of candidate rows, then top-k.  See select.hip.
 struct SelectArgs {
@@ -343,7 +346,23 @@ struct GemmArgs {
   // host-side: when set (QKV, bf16, no split-K), launch_gemm runs the
   // re-alignment it describes in the same launch
   const ShiftFuse* shift;
+  // gate/up only: A is in the step-major layout of act_packed_index (see
+  // gemm_gateup_packed_a)
+  int a_packed;
 };
+
+// Step-major layout of a bf16 activation matrix [rows][d] (d a multiple of
+// 32) for the gate/up projection: 256-row tiles, each a run of 32-column
+// steps, each step the tile's 256 rows x 32 columns row by row (16 KB), so
+// that one K step of a row tile is contiguous.  Index of element (i, c);
+// act_packed_rows(rows) rows are stored (the last tile padded).
+__host__ __device__ inline int64_t act_packed_index(int i, int c, int d) {
+  return (((int64_t)(i >> 8) * (d >> 5) + (c >> 5)) * 256 + (i & 255)) * 32 + (c & 31);
+}
+__host__ __device__ inline int act_packed_rows(int rows) { return (rows + 255) / 256 * 256; }
+// whether the bf16 gate/up projection over K = d takes its A operand in the
+// step-major layout (then the MLP RMSNorm writes it so)
+bool gemm_gateup_packed_a(int dtype, int K);
 
 int gemm_bn(int dtype);                               // N tile width
 int gemm_splits(int dtype, int N_tiles, int K);       // split-K choice (independent of M)
@@ -358,11 +377,12 @@ bool gemm_fuses_shift(int dtype, const GemmArgs& g);
 hipError_t launch_epilogue_only(const GemmArgs& g, hipStream_t s);
 int epilogue_ld(int N);
 // ... the RESID epilogue into fp32 h followed by the RMSNorm of h into hn
-hipError_t launch_resid_norm_only(const GemmArgs& g, const float* gain, float eps, void* hn, hipStream_t s);
+hipError_t launch_resid_norm_only(const GemmArgs& g, const float* gain, float eps, void* hn, hipStream_t s,
+                                  bool hn_packed = false);
 // A residual projection into fp32 rows (epi.out) followed by the RMSNorm of
 // those rows into hn (the cache dtype), fused after split-K when possible.
 hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g, const float* gain, float eps, void* hn,
-                                  hipStream_t s);
+                                  hipStream_t s, bool hn_packed = false);
 
 // ---------------------------------------------------------------------------
 // Attention of selected rows over the cache.

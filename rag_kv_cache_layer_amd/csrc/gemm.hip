@@ -653,6 +653,10 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
 #ifndef CB_BIG_NSTAGE
 #define CB_BIG_NSTAGE 4
 #endif
+// gate/up on the software-pipelined four-wave kernel instead
+#ifndef CB_GATEUP_W4
+#define CB_GATEUP_W4 1
+#endif
 constexpr int LBM = 256, LBN = CB_BIG_BN, LBK = 32, LNS = CB_BIG_NSTAGE, LCLD = LBN + 4;
 constexpr int kLW = CB_BIG_WAVES;                    // waves per workgroup
 static_assert(LBN == 224 || LBN == 256, "large tile: 224 or 256 columns");
@@ -840,6 +844,166 @@ __global__ __launch_bounds__(kLNT, 1) void gemm_bf16_big_kernel(GemmArgs g, int 
   }
 }
 
+// Four waves of 128 x 128 on the 256 x 256 gate/up tile (one wave per SIMD),
+// software-pipelined: in the step for K step `it` a wave first issues the
+// LDS fragment reads of step it + 1 (into the other register set), then the
+// 64 MFMAs of step it from the fragments read one step earlier, with the
+// direct-to-LDS loads of step it + 3 between the MFMA rows.  The barrier at
+// the top of a step therefore waits for step it + 1's loads, and the LDS
+// reads never stand between a barrier and the matrix cores.  Per step and
+// CU this moves 64 KB of fragment reads and 32 KB of loads through LDS
+// against 96 KB + 32 KB for eight waves of 128 x 64.
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt, int ntiles) {
+  constexpr int TBN = 256, NS = 4, CLD = TBN + 4;
+  constexpr int kStage = (LBM + TBN) * LBK * 2;                 // 32 KB
+  constexpr int kSmem = NS * kStage > 128 * CLD * 4 ? NS * kStage : 128 * CLD * 4;
+  constexpr int kBlocksA = LBM / 16;                             // 16 A blocks, then 16 B blocks
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = id % mt, tn = id / mt;
+  const int m0 = tm * LBM;
+  const int M = g.M, K = g.K;
+  const int nk = K / LBK;   // whole steps (checked by the host)
+
+  // DMA plan: wave w fills blocks w + 4 j (j < 8) of a stage: A blocks for
+  // j < 4, B blocks for j >= 4.  A block's byte offset for the step at k0 is
+  // base[j] + k0 * mul[j] (2 bytes per element of a row-major operand; one
+  // 16 KB block per step in the packed layout); rows past the operand start
+  // past the buffer's end and load as zero, so the main loop has no branch.
+  const uint32_t kOOB = 0x80000000u;
+  const int rl = rho16_inv(lane >> 2);
+  const int lcol = ((lane & 3) ^ ((rl >> 1) & 3)) * 8;
+  const bool packed = g.B.mode == 1 && g.B.packed != nullptr;
+  __amdgpu_buffer_rsrc_t rs[8];
+  uint32_t base[8];
+  int mul[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int blk = w + 4 * j;
+    if (blk < kBlocksA && g.a_packed) {
+      // A in the step-major layout: one 16 KB block per (row tile, step);
+      // the padded rows of the last tile only feed output rows past M
+      const int row = blk * 16 + rl;
+      rs[j] = make_rsrc(g.A, (uint32_t)((int64_t)act_packed_rows(M) * K * 2));
+      base[j] = (uint32_t)(tm * nk) * (LBM * 64) + (uint32_t)(row * 64 + lcol * 2);
+      mul[j] = LBM * 64 / LBK;
+    } else if (blk < kBlocksA) {
+      const int row = blk * 16 + rl;
+      rs[j] = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
+      base[j] = (m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB) + lcol * 2;
+      mul[j] = 2;
+    } else if (packed) {
+      const int r0 = (blk - kBlocksA) * 16;
+      rs[j] = make_rsrc(g.B.packed, (uint32_t)pack_gateup_bytes(g.B.n_feat, K));
+      base[j] = (uint32_t)(tn * nk) * (TBN * 64) + (uint32_t)((r0 + rl) * 64 + lcol * 2);
+      mul[j] = TBN * 64 / LBK;
+    } else {
+      const int r0 = (blk - kBlocksA) * 16;
+      const int f = tn * (TBN / 2) + (r0 % (TBN / 2)) + rl;
+      // B blocks 0..7 of the tile are gate rows, 8..15 up rows
+      rs[j] = make_rsrc(r0 < TBN / 2 ? g.B.p0 : g.B.p1, (uint32_t)((int64_t)g.B.n_feat * K * 2));
+      base[j] = (f < g.B.n_feat ? (uint32_t)((int64_t)f * K * 2) : kOOB) + lcol * 2;
+      mul[j] = 2;
+    }
+  }
+  // a step past the last one loads zeros (offset past every buffer) into a
+  // stage that is never read again, so the issue needs no branch either
+  auto issue_block = [&](int stage, int k0, int j) {
+    const uint32_t o = (base[j] + (uint32_t)(k0 * mul[j])) | ((uint32_t)(k0 >= K) << 31);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kStage + (w + 4 * j) * 1024), 16, o,
+                                             0, 0, 0);
+  };
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // the 256 accumulator registers live in the AGPR file (an empty asm
+      // statement with an AGPR operand places them there), which leaves the
+      // 256 VGPRs to the two fragment sets and the addressing
+      asm volatile("" : "+a"(acc[i][j]));
+    }
+  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const int fr = lane & 15, fc = lane >> 4;
+  bf16x8_t fa[2][8], fb[2][8];
+  auto read_frags = [&](int stage, int set) {
+    const char* sa = smem + stage * kStage;
+    const char* sb = sa + LBM * LBK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + j * 16 + fr, fc));
+  };
+
+  // prologue: steps 0..NS-1 in flight, step 0's fragments in set 0
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_block(st, st * LBK, j);
+  }
+  CB_WAIT_VMCNT(8 * (NS - 1));
+  CB_BARRIER();
+  read_frags(0, 0);
+
+  // main loop, unrolled by the ring depth so every LDS address and register
+  // set is static (the host launches this kernel only when NS divides the
+  // step count).  Step it's stage is free once every wave has read its
+  // fragments (during step it - 1, complete at the barrier of step it), so
+  // step it + NS is loaded into it from then on: NS steps in flight.
+  for (int it0 = 0; it0 < nk; it0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int it = it0 + u;
+      const int cur = u & 1;   // NS is even: the fragment set of step it is it & 1
+      // this wave's loads of step it + 1 landed once only those of steps
+      // it + 2 .. it + NS - 1 are outstanding; then every wave's have (barrier)
+      CB_WAIT_VMCNT(8 * (NS - 2));
+      CB_BARRIER();
+      // the next step's fragments (past the last step: unused) are read two
+      // at a time between the MFMA rows, so the four waves' reads do not
+      // queue up at the LDS in front of their first MFMAs
+      const char* na = smem + ((u + 1) % NS) * kStage;
+      const char* nb = na + LBM * LBK * 2;
+      const int nk0 = (it + NS) * LBK;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(na + swz32(wm + i * 16 + fr, fc));
+        fb[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(nb + swz32(wn + i * 16 + fr, fc));
+        issue_block(u, nk0, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  CB_WAIT_VMCNT(0);
+  __syncthreads();
+
+  // epilogue in two halves of 128 rows
+  float* Cs = (float*)smem;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm / 128 == half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Cs[(i * 16 + fc * 4 + v) * CLD + wn + j * 16 + fr] = acc[i][j][v];
+    }
+    __syncthreads();
+    run_epilogue<bf16_t, 128, TBN, 256, KIND>(g.epi, g.B, Cs, CLD, m0 + half * 128, tn, M, g.N);
+    __syncthreads();
+  }
+}
+
 // Split-K finish: one thread per 8 output columns of a row adds the split
 // partials in split order straight from memory and applies the epilogue.
 // 16 rows x one 128-column tile per workgroup; no LDS staging.
@@ -904,7 +1068,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, int nt
 constexpr int kResidNormGroups = 4;  // 8-column groups per thread: rows up to 256 * 8 * 4 = 8192 wide
 
 __global__ __launch_bounds__(256) void resid_norm_kernel(GemmArgs g, int ntiles, const float* __restrict__ gain,
-                                                         float eps, bf16_t* __restrict__ hn) {
+                                                         float eps, bf16_t* __restrict__ hn, int hn_packed) {
   __shared__ float red[4];
   const int gm = blockIdx.x;
   const int ldp = ntiles * BN;
@@ -946,7 +1110,7 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(GemmArgs g, int ntiles,
       load8(gain + c, gg);
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = (h[i][j] / rs) * gg[j];
-      store8(hn + (int64_t)gm * d + c, o);
+      store8(hn + (hn_packed ? act_packed_index(gm, c, d) : (int64_t)gm * d + c), o);
     }
   }
 }
@@ -1118,29 +1282,33 @@ hipError_t launch_epilogue_only(const GemmArgs& g0, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_resid_norm_only(const GemmArgs& g, const float* gain, float eps, void* hn, hipStream_t s) {
+hipError_t launch_resid_norm_only(const GemmArgs& g, const float* gain, float eps, void* hn, hipStream_t s,
+                                  bool hn_packed) {
   if (g.M <= 0) return hipSuccess;
+  if (hn_packed && g.N % 32) return hipErrorInvalidValue;
   if (g.epi.kind != EPI_RESID || !g.epi.out_f32 || g.N % 8 || g.N > 256 * 8 * kResidNormGroups ||
       g.epi.ld_out != g.N) {
     hipError_t e = launch_epilogue_only(g, s);
     if (e != hipSuccess) return e;
-    return launch_rmsnorm(CB_BF16, true, g.epi.out, g.M, nullptr, nullptr, gain, hn, g.M, g.N, eps, s);
+    return launch_rmsnorm(CB_BF16, true, g.epi.out, g.M, nullptr, nullptr, gain, hn, g.M, g.N, eps, s, hn_packed);
   }
   LaunchScope ls("resid_norm", s);
-  resid_norm_kernel<<<g.M, 256, 0, s>>>(g, gemm_n_tiles(CB_BF16, g.B, g.N), gain, eps, (bf16_t*)hn);
+  resid_norm_kernel<<<g.M, 256, 0, s>>>(g, gemm_n_tiles(CB_BF16, g.B, g.N), gain, eps, (bf16_t*)hn, hn_packed);
   return hipGetLastError();
 }
 
 int epilogue_ld(int N) { return (N + BN - 1) / BN * BN; }
 
 hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g0, const float* gain, float eps, void* hn,
-                                  hipStream_t s) {
+                                  hipStream_t s, bool hn_packed) {
   if (g0.M <= 0) return hipSuccess;
+  if (hn_packed && (dtype != CB_BF16 || g0.N % 32)) return hipErrorInvalidValue;
   if (dtype != CB_BF16 || g0.splits <= 1 || g0.epi.kind != EPI_RESID || !g0.epi.out_f32 || g0.N % 8 ||
       g0.N > 256 * 8 * kResidNormGroups || g0.epi.ld_out != g0.N) {
     hipError_t e = launch_gemm(dtype, g0, s);
     if (e != hipSuccess) return e;
-    return launch_rmsnorm(dtype, true, g0.epi.out, g0.M, nullptr, nullptr, gain, hn, g0.M, g0.N, eps, s);
+    return launch_rmsnorm(dtype, true, g0.epi.out, g0.M, nullptr, nullptr, gain, hn, g0.M, g0.N, eps, s,
+                          hn_packed);
   }
   GemmArgs g = g0;
   const int ntiles = gemm_n_tiles(dtype, g.B, g.N);
@@ -1152,8 +1320,12 @@ hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g0, const float* ga
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   LaunchScope ls("resid_norm", s);
-  resid_norm_kernel<<<g.M, 256, 0, s>>>(g, ntiles, gain, eps, (bf16_t*)hn);
+  resid_norm_kernel<<<g.M, 256, 0, s>>>(g, ntiles, gain, eps, (bf16_t*)hn, hn_packed);
   return hipGetLastError();
+}
+
+bool gemm_gateup_packed_a(int dtype, int K) {
+  return dtype == CB_BF16 && CB_GATEUP_W4 && LBN == 256 && K % (4 * LBK) == 0;
 }
 
 bool gemm_fuses_shift(int dtype, const GemmArgs& g) {
@@ -1170,8 +1342,13 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
     const int mt = (g.M + LBM - 1) / LBM;
     g.N = nt * LBN;
     g.splits = 1;
+    const bool w4 = gemm_gateup_packed_a(dtype, g.K);
+    if (g.a_packed && !w4) return hipErrorInvalidValue;
     LaunchScope ls("gemm_gateup", s);
-    gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), kLNT, 0, s>>>(g, mt, nt);
+    if (w4)
+      gemm_bf16_w4_kernel<EPI_SWIGLU><<<dim3(mt * nt), 256, 0, s>>>(g, mt, nt);
+    else
+      gemm_bf16_big_kernel<EPI_SWIGLU><<<dim3(mt * nt), kLNT, 0, s>>>(g, mt, nt);
     return hipGetLastError();
   }
   const int ntiles = gemm_n_tiles(dtype, g.B, g.N);

@@ -9,17 +9,18 @@ namespace cb {
 
 namespace {
 
+// (packed: row i goes to the step-major layout of act_packed_index)
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const Tin* __restrict__ x, int n_src, const int* m1,
                                                       const int* m2, const float* __restrict__ g,
-                                                      Tout* __restrict__ out, int d, float eps) {
+                                                      Tout* __restrict__ out, int d, float eps, int packed) {
   __shared__ float red[4];
   const int i = blockIdx.x;
   const int src = map_row(i, m1, m2);
-  Tout* orow = out + (int64_t)i * d;
+  auto dst = [&](int c) { return out + (packed ? act_packed_index(i, c, d) : (int64_t)i * d + c); };
   if (src < 0 || src >= n_src) {  // invalid index: zero row, no out-of-bounds read
     const float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) store8(orow + c, z);
+    for (int c = threadIdx.x * 8; c < d; c += 256 * 8) store8(dst(c), z);
     return;
   }
   const Tin* xr = x + (int64_t)src * d;
@@ -43,23 +44,27 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const Tin* __restrict__ x,
     load8(g + c, gg);
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = (v[j] / rs) * gg[j];
-    store8(orow + c, o);
+    store8(dst(c), o);
   }
 }
 
 }  // namespace
 
 hipError_t launch_rmsnorm(int dtype, bool x_f32, const void* x, int n_src, const int* m1, const int* m2,
-                          const float* g, void* out, int rows, int d, float eps, hipStream_t s) {
+                          const float* g, void* out, int rows, int d, float eps, hipStream_t s, bool packed_out) {
   if (rows <= 0) return hipSuccess;
+  if (packed_out && (dtype != CB_BF16 || d % 32)) return hipErrorInvalidValue;
+  const int pk = packed_out ? 1 : 0;
   LaunchScope ls("rmsnorm", s);
   if (dtype == CB_BF16) {
     if (x_f32)
-      rmsnorm_kernel<float, bf16_t><<<rows, 256, 0, s>>>((const float*)x, n_src, m1, m2, g, (bf16_t*)out, d, eps);
+      rmsnorm_kernel<float, bf16_t>
+          <<<rows, 256, 0, s>>>((const float*)x, n_src, m1, m2, g, (bf16_t*)out, d, eps, pk);
     else
-      rmsnorm_kernel<bf16_t, bf16_t><<<rows, 256, 0, s>>>((const bf16_t*)x, n_src, m1, m2, g, (bf16_t*)out, d, eps);
+      rmsnorm_kernel<bf16_t, bf16_t>
+          <<<rows, 256, 0, s>>>((const bf16_t*)x, n_src, m1, m2, g, (bf16_t*)out, d, eps, pk);
   } else {
-    rmsnorm_kernel<float, float><<<rows, 256, 0, s>>>((const float*)x, n_src, m1, m2, g, (float*)out, d, eps);
+    rmsnorm_kernel<float, float><<<rows, 256, 0, s>>>((const float*)x, n_src, m1, m2, g, (float*)out, d, eps, 0);
   }
   return hipGetLastError();
 }
