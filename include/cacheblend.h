@@ -151,12 +151,13 @@ cb_status cb_filter_schedule(int32_t n_layers, int32_t r_first_e4, int32_t r_las
                              int32_t n_ctx, int32_t n_cand, int32_t* k_out);
 
 /* One-time weight repack (a model-load step, not part of a request).  The
- * gate/up projection streams 256-row tiles (128 gate rows, then the same 128
+ * gate/up projection streams 224-row tiles (112 gate rows, then the same 112
  * up rows) in 32-element K steps; cb_pack_gateup stores W_gate and W_up (bf16
  * device [ffn][d] each) in exactly that order, tile by tile and step by step,
- * each (tile, step) block of 256 rows x 64 bytes contiguous, rows past ffn
+ * each (tile, step) block of 224 rows x 64 bytes contiguous, rows past ffn
  * and K past d zero, so that every load of the kernel reads contiguous
- * memory.  packed: device, cb_pack_gateup_size(cfg) bytes, 16-byte aligned.
+ * memory (d_model a multiple of 128; otherwise the projection reads the
+ * row-major weights).  packed: device, cb_pack_gateup_size(cfg) bytes, 16-byte aligned.
  * CB_ERR_UNSUPPORTED for fp32 configs (the fp32 path does not use it). */
 size_t cb_pack_gateup_size(const cb_layer_config* cfg);
 cb_status cb_pack_gateup(const cb_layer_config* cfg, const void* w_gate, const void* w_up,

@@ -288,11 +288,14 @@ struct BOperand {
   // order (see launch_pack_gateup); p0/p1 are then not read
   const void* packed;
 };
-// The gate/up operand in the order the 256-wide gated kernel streams it: for
-// each tile of kGateupTile/2 features and each kGateupStep-element K step,
-// the tile's gate rows then the same up rows, kGateupStep elements each, as
-// one contiguous block; rows past n_feat and K past K are zero.
-constexpr int kGateupTile = 256, kGateupStep = 32;
+// The gate/up operand in the order the gated kernel streams it: for each
+// tile of kGateupTile/2 features and each kGateupStep-element K step, the
+// tile's gate rows then the same up rows, kGateupStep elements each, as one
+// contiguous block; rows past n_feat and K past K are zero.
+#ifndef CB_W4_BN
+#define CB_W4_BN 224
+#endif
+constexpr int kGateupTile = CB_W4_BN, kGateupStep = 32;
 __host__ __device__ inline size_t pack_gateup_bytes(int n_feat, int K) {
   const size_t tiles = (size_t)(n_feat + kGateupTile / 2 - 1) / (kGateupTile / 2);
   const size_t nk = (size_t)(K + kGateupStep - 1) / kGateupStep;

@@ -853,12 +853,18 @@ __global__ __launch_bounds__(kLNT, 1) void gemm_bf16_big_kernel(GemmArgs g, int 
 // reads never stand between a barrier and the matrix cores.  Per step and
 // CU this moves 64 KB of fragment reads and 32 KB of loads through LDS
 // against 96 KB + 32 KB for eight waves of 128 x 64.
+// TBN = kGateupTile columns: 256, or 224 (the 8B layer's 14336 features then
+// make 2 x 128 = 256 workgroups, one per CU; its waves are 128 x 112 and a
+// stage's two missing B blocks are loads past the buffer's end into padding).
 template <int KIND>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt, int ntiles) {
-  constexpr int TBN = 256, NS = 4, CLD = TBN + 4;
-  constexpr int kStage = (LBM + TBN) * LBK * 2;                 // 32 KB
+  constexpr int TBN = kGateupTile, NS = 4, CLD = TBN + 4;
+  constexpr int FB = TBN / 32;                                   // B fragments per wave (8 or 7)
+  constexpr int kStage = (LBM + 256) * LBK * 2;                 // 32 KB (padded for TBN = 224)
   constexpr int kSmem = NS * kStage > 128 * CLD * 4 ? NS * kStage : 128 * CLD * 4;
-  constexpr int kBlocksA = LBM / 16;                             // 16 A blocks, then 16 B blocks
+  constexpr int kBlocksA = LBM / 16;                             // 16 A blocks, then TBN/16 B blocks
+  constexpr int kBlocks = kBlocksA + TBN / 16;
+  static_assert(TBN == 256 || TBN == 224, "gate/up tile width");
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -895,6 +901,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt
       rs[j] = make_rsrc(g.A, (uint32_t)((int64_t)M * K * 2));
       base[j] = (m0 + row < M ? (uint32_t)((int64_t)(m0 + row) * K * 2) : kOOB) + lcol * 2;
       mul[j] = 2;
+    } else if (blk >= kBlocks) {
+      // padding block of a 224-wide tile: a load past every buffer (zeros)
+      rs[j] = make_rsrc(g.A, 0u);
+      base[j] = kOOB;
+      mul[j] = 0;
     } else if (packed) {
       const int r0 = (blk - kBlocksA) * 16;
       rs[j] = make_rsrc(g.B.packed, (uint32_t)pack_gateup_bytes(g.B.n_feat, K));
@@ -917,27 +928,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt
                                              0, 0, 0);
   };
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][FB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < FB; ++j) {
       acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       // the 256 accumulator registers live in the AGPR file (an empty asm
       // statement with an AGPR operand places them there), which leaves the
       // 256 VGPRs to the two fragment sets and the addressing
       asm volatile("" : "+a"(acc[i][j]));
     }
-  const int wm = (w >> 1) * 128, wn = (w & 1) * 128;
+  const int wm = (w >> 1) * 128, wn = (w & 1) * (TBN / 2);
   const int fr = lane & 15, fc = lane >> 4;
-  bf16x8_t fa[2][8], fb[2][8];
+  bf16x8_t fa[2][8], fb[2][FB];
   auto read_frags = [&](int stage, int set) {
     const char* sa = smem + stage * kStage;
     const char* sb = sa + LBM * LBK * 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) fa[set][i] = *reinterpret_cast<const bf16x8_t*>(sa + swz32(wm + i * 16 + fr, fc));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + j * 16 + fr, fc));
+    for (int j = 0; j < FB; ++j) fb[set][j] = *reinterpret_cast<const bf16x8_t*>(sb + swz32(wn + j * 16 + fr, fc));
   };
 
   // prologue: steps 0..NS-1 in flight, step 0's fragments in set 0
@@ -973,11 +984,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < FB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         fa[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(na + swz32(wm + i * 16 + fr, fc));
-        fb[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(nb + swz32(wn + i * 16 + fr, fc));
+        if (i < FB) fb[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(nb + swz32(wn + i * 16 + fr, fc));
         issue_block(u, nk0, i);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -994,7 +1005,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < FB; ++j)
 #pragma unroll
           for (int v = 0; v < 4; ++v) Cs[(i * 16 + fc * 4 + v) * CLD + wn + j * 16 + fr] = acc[i][j][v];
     }
@@ -1325,7 +1336,7 @@ hipError_t launch_gemm_resid_norm(int dtype, const GemmArgs& g0, const float* ga
 }
 
 bool gemm_gateup_packed_a(int dtype, int K) {
-  return dtype == CB_BF16 && CB_GATEUP_W4 && LBN == 256 && K % (4 * LBK) == 0;
+  return dtype == CB_BF16 && CB_GATEUP_W4 && K % (4 * LBK) == 0;
 }
 
 bool gemm_fuses_shift(int dtype, const GemmArgs& g) {
@@ -1337,12 +1348,13 @@ hipError_t launch_gemm(int dtype, const GemmArgs& g0, hipStream_t s) {
   if (g0.M <= 0) return hipSuccess;
   GemmArgs g = g0;
   if (dtype == CB_BF16 && g.B.mode == 1) {
-    // gated pair (gate/up): 256x256 tiles, no split
-    const int nt = (g.B.n_feat + LBN / 2 - 1) / (LBN / 2);
-    const int mt = (g.M + LBM - 1) / LBM;
-    g.N = nt * LBN;
-    g.splits = 1;
+    // gated pair (gate/up): 256-row tiles, no split
     const bool w4 = gemm_gateup_packed_a(dtype, g.K);
+    const int tbn = w4 ? kGateupTile : LBN;
+    const int nt = (g.B.n_feat + tbn / 2 - 1) / (tbn / 2);
+    const int mt = (g.M + LBM - 1) / LBM;
+    g.N = nt * tbn;
+    g.splits = 1;
     if (g.a_packed && !w4) return hipErrorInvalidValue;
     LaunchScope ls("gemm_gateup", s);
     if (w4)

@@ -299,7 +299,7 @@ def test_validate_switch(cblib):
 
 def test_pack_gateup_argument_errors(cblib):
     L, cfg = cblib, _cfg()
-    assert int(L.cb_pack_gateup_size(ctypes.byref(cfg))) == 8 * 16 * 256 * 64   # 1024/128 tiles x 512/32 steps
+    assert int(L.cb_pack_gateup_size(ctypes.byref(cfg))) == 10 * 16 * 224 * 64  # ceil(1024/112) tiles x 512/32 steps
     assert int(L.cb_pack_gateup_size(ctypes.byref(_cfg(dtype="f32")))) == 0
     assert L.cb_pack_gateup(ctypes.byref(_cfg(dtype="f32")), FAKE, FAKE, FAKE, None) == 5
     assert L.cb_pack_gateup(ctypes.byref(cfg), None, FAKE, FAKE, None) == 1

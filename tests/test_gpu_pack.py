@@ -2,7 +2,7 @@
 re-layout of the weights (bit for bit), and the layer calls with the packed
 copy against the same calls on the row-major weights (every output bit for
 bit: only the addresses the kernel loads from change, not the order of any
-sum).  Ragged cases: an FFN width that is not a multiple of the 128-feature
+sum).  Ragged cases: an FFN width that is not a multiple of the 112-feature
 tile, and a model width that is not a multiple of the 32-element K step."""
 import numpy as np
 import pytest
@@ -17,20 +17,23 @@ MED64 = synth.scaled(synth.PRESETS["llama8b_layer"], 1024, 16, 4, 64, 2776, [100
 ODD_D = synth.scaled(synth.PRESETS["llama8b_layer"], 520, 8, 2, 64, 392, [40, 33, 50], 7)
 
 
+TILE = 112   # features per gate/up tile (224 rows: the gate rows, then the same up rows)
+
+
 def _layout(gate, up, K):
-    """numpy: tiles of 128 features x 32-element steps, 128 gate rows then the
-    same 128 up rows per (tile, step) block, zero past the ends."""
+    """numpy: tiles of 112 features x 32-element steps, 112 gate rows then the
+    same 112 up rows per (tile, step) block, zero past the ends."""
     F_, = gate.shape[:1]
-    tiles, nk = -(-F_ // 128), -(-K // 32)
-    out = np.zeros((tiles, nk, 256, 32), np.uint16)
-    g = np.zeros((tiles * 128, nk * 32), np.uint16)
+    tiles, nk = -(-F_ // TILE), -(-K // 32)
+    out = np.zeros((tiles, nk, 2 * TILE, 32), np.uint16)
+    g = np.zeros((tiles * TILE, nk * 32), np.uint16)
     u = np.zeros_like(g)
     g[:F_, :K] = gate
     u[:F_, :K] = up
     for t in range(tiles):
         for s in range(nk):
-            out[t, s, :128] = g[t * 128:(t + 1) * 128, s * 32:(s + 1) * 32]
-            out[t, s, 128:] = u[t * 128:(t + 1) * 128, s * 32:(s + 1) * 32]
+            out[t, s, :TILE] = g[t * TILE:(t + 1) * TILE, s * 32:(s + 1) * 32]
+            out[t, s, TILE:] = u[t * TILE:(t + 1) * TILE, s * 32:(s + 1) * 32]
     return out.reshape(-1)
 
 
