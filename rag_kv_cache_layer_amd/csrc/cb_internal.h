@@ -102,6 +102,19 @@ struct ReqTable {
 
 // s_waitcnt vmcnt(n) lgkmcnt(0): this wave's LDS DMA up to the n most recent
 // loads has landed and its LDS reads have returned.
+// Cache policy bits of the GEMMs' direct-to-LDS operand loads.  The weight
+// rows are read once per launch (each by the few workgroups of one output
+// column block, close together in time), so they are loaded non-temporal
+// (bit 1, nt): the L2 and the Infinity Cache then keep the activation rows,
+// which every output column block reads again, and the split-K partials
+// that the finishing kernels read next.  The activation rows use the default.
+#ifndef CB_W_AUX
+#define CB_W_AUX 2
+#endif
+#ifndef CB_A_AUX
+#define CB_A_AUX 0
+#endif
+
 #define CB_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
 // Workgroup barrier without a memory fence (a fence would drain the DMA ring);
 // the empty asm statements keep the compiler from moving LDS accesses across it.

@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(Fp8GemmArgs g, int mt,
     const bool kin = kk < ke;
     const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk : kOOB;
     const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, CB_A_AUX);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, CB_W_AUX);
   };
   auto issue = [&](int stage, int k0) {
 #pragma unroll
@@ -273,8 +273,13 @@ __global__ __launch_bounds__(512, 1) void gemm_fp8_big_kernel(Fp8GemmArgs g, int
     const int blk = w + 8 * j;
     const int kk = k0 + lcol[j];
     const uint32_t o = (kk < K && off[j] != kOOB) ? off[j] + kk : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(blk < kQLBlocksA ? ra : rb,
-                                             (lds_void*)(smem + stage * kQLStage + blk * 1024), 16, o, 0, 0, 0);
+    static_assert(kQLBlocksA % 8 == 0, "block w + 8 j is an activation block exactly when 8 j < kQLBlocksA");
+    if (8 * j < kQLBlocksA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(smem + stage * kQLStage + blk * 1024), 16, o, 0, 0,
+                                               CB_A_AUX);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(smem + stage * kQLStage + blk * 1024), 16, o, 0, 0,
+                                               CB_W_AUX);
   };
 
   f32x4_t acc[8][4];

@@ -498,8 +498,8 @@ __global__ __launch_bounds__(256, CB_GEMM_MINBLOCKS) void gemm_bf16_kernel(GemmA
     const bool kin = kk < ke;
     const uint32_t oa = (kin && aoff[j] != kOOB) ? aoff[j] + kk * 2 : kOOB;
     const uint32_t ob = (kin && boff[j] != kOOB) ? boff[j] + kk * 2 : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + grp * 1024), 16, oa, 0, 0, CB_A_AUX);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[j], (lds_void*)(sb + grp * 1024), 16, ob, 0, 0, CB_W_AUX);
   };
   auto issue = [&](int stage, int k0) {
 #pragma unroll
@@ -924,8 +924,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs g, int mt
   // stage that is never read again, so the issue needs no branch either
   auto issue_block = [&](int stage, int k0, int j) {
     const uint32_t o = (base[j] + (uint32_t)(k0 * mul[j])) | ((uint32_t)(k0 >= K) << 31);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kStage + (w + 4 * j) * 1024), 16, o,
-                                             0, 0, 0);
+    if (j < 4)   // blocks w + 4 j < 16: activation rows
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kStage + (w + 4 * j) * 1024), 16, o,
+                                               0, 0, CB_A_AUX);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kStage + (w + 4 * j) * 1024), 16, o,
+                                               0, 0, CB_W_AUX);
   };
 
   f32x4_t acc[8][FB];
