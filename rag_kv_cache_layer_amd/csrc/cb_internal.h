@@ -105,9 +105,11 @@ struct ReqTable {
 // Cache policy bits of the GEMMs' direct-to-LDS operand loads.  The weight
 // rows are read once per launch (each by the few workgroups of one output
 // column block, close together in time), so they are loaded non-temporal
-// (bit 1, nt): the L2 and the Infinity Cache then keep the activation rows,
-// which every output column block reads again, and the split-K partials
-// that the finishing kernels read next.  The activation rows use the default.
+// (bit 1, nt), which leaves the caches to the activation rows that every
+// output column block reads again and to the split-K partials that the
+// finishing kernels read next (measured: the same L2 fetch bytes, a faster
+// step, and the finishing kernels faster too, i.e. the memory-side Infinity
+// Cache keeps more of those).  The activation rows use the default policy.
 #ifndef CB_W_AUX
 #define CB_W_AUX 2
 #endif
