@@ -228,12 +228,13 @@ __device__ void qkv_tile_epilogue(const EpiParams& e, const float* Cs, int cld, 
       }
     }
   }
+  float contrib[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int rl = p * rpp + lr;
     const int gm = m0 + rl;
     const int r = crow[p];
-    float contrib = 0.f;
+    contrib[p] = 0.f;
     if (r >= 0) {
       const float* row = Cs + rl * cld;
       float v[8];
@@ -272,17 +273,25 @@ __device__ void qkv_tile_epilogue(const EpiParams& e, const float* Cs, int cld, 
 #pragma unroll
             for (int j = 0; j < 8; ++j) old[j] = Elem<T>::rnd(rot[j]);
           }
-          contrib = dev_add8(rv, old, contrib);
+          contrib[p] = dev_add8(rv, old, 0.f);
         }
         store8(kp, rv);
       } else {
         store8((T*)e.v_cache + (int64_t)r * e.kv_dim + (c - e.q_dim - e.kv_dim), v);
       }
     }
-    if (k_tile) {
-      // fixed-order reduction over the tpr consecutive lanes of this row
-      for (int o = tpr / 2; o > 0; o >>= 1) contrib += __shfl_xor(contrib, o);
-      if ((tid % tpr) == 0 && gm < M) e.dev_part[(int64_t)(tn - e.k_tile0) * M + gm] = contrib;
+  }
+  if (k_tile) {
+    // fixed-order reduction over the tpr consecutive lanes of each row, the
+    // rows' cross-lane steps interleaved so that their latencies overlap
+    for (int o = tpr / 2; o > 0; o >>= 1) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) contrib[p] += __shfl_xor(contrib[p], o);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int gm = m0 + p * rpp + lr;
+      if ((tid % tpr) == 0 && gm < M) e.dev_part[(int64_t)(tn - e.k_tile0) * M + gm] = contrib[p];
     }
   }
 }
