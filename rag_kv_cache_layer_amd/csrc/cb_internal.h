@@ -100,8 +100,6 @@ struct ReqTable {
   int lo[kMaxReq], hi[kMaxReq];   // QKV: deviation for cache rows in [lo, hi)
 };
 
-// s_waitcnt vmcnt(n) lgkmcnt(0): this wave's LDS DMA up to the n most recent
-// loads has landed and its LDS reads have returned.
 // Cache policy bits of the GEMMs' direct-to-LDS operand loads.  The weight
 // rows are read once per launch (each by the few workgroups of one output
 // column block, close together in time), so they are loaded non-temporal
@@ -117,6 +115,8 @@ struct ReqTable {
 #define CB_A_AUX 0
 #endif
 
+// s_waitcnt vmcnt(n) lgkmcnt(0): this wave's LDS DMA up to the n most recent
+// loads has landed and its LDS reads have returned.
 #define CB_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0070)
 // Workgroup barrier without a memory fence (a fence would drain the DMA ring);
 // the empty asm statements keep the compiler from moving LDS accesses across it.

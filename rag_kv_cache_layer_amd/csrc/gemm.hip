@@ -774,7 +774,13 @@ __global__ __launch_bounds__(kLNT, 1) void gemm_bf16_big_kernel(GemmArgs g, int 
       const int kk = k0 + lcol;
       o = (kk < K && off[j] != kOOB) ? off[j] + kk * 2 : kOOB;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kLStage + dst[j]), 16, o, 0, 0, 0);
+    static_assert(kLBlocksA % kLW == 0, "block w + kLW j is a weight block exactly when kLW j >= kLBlocksA");
+    if (kLW * j >= kLBlocksA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kLStage + dst[j]), 16, o, 0, 0,
+                                               CB_W_AUX);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j], (lds_void*)(smem + stage * kLStage + dst[j]), 16, o, 0, 0,
+                                               CB_A_AUX);
   };
   auto issue = [&](int stage, int k0) {
 #pragma unroll
