@@ -151,10 +151,14 @@ def test_select_then_blend_calls(p, fold, gains):
     want = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_in, case["hidden"][s_in], k, store=st,
                              keep=keep)
     _check_blend(p, case, got, want, s_in)
-    # free-running agreement of the two selections (reported, not gated)
+    # free-running agreement of the two selections: the same set in fp32;
+    # in bf16 rows whose deviations tie within rounding may swap places
+    # (0.96-1.0 on these cases)
     own = blend.blend_layer(case["w"], p, case["k"], case["v"], n_ctx, s_in, case["hidden"][s_in], k, store=st)
     a, b = set(own["s_out"][:k].tolist()), set(got["s_out"][:k].tolist())
-    print(f"\n{p.name}: jaccard(GPU, oracle selection) = {len(a & b) / max(len(a | b), 1):.4f}")
+    jac = len(a & b) / max(len(a | b), 1)
+    print(f"\n{p.name}: jaccard(GPU, oracle selection) = {jac:.4f}")
+    assert jac >= (1.0 if p.dtype == "f32" else 0.9)
     # blend call: recompute only the kept rows S on the precomputed (shifted)
     # cache, as the next layer of a stack does with the set this layer chose
     s2 = want["s_out"]
